@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+the dense causal prefill (B=4, H=16, S=2048, d=128, bf16) through mxfa_fwd,
+and the latent-KV split decode (batch 128, q_len 4, 16 heads, 576/512,
+kv_len 8192, bf16) through mxfa_decode_splitkv. Inputs are generated with the
+seeded recipe of the ``workloads`` module and are resident in HBM before the
+timed region. Each call is timed with HIP events on the stream it is launched
+on, over ``--steps`` launches after ``--warmup`` untimed ones.
+
+Prints ONE JSON line. ``value`` is the prefill's algorithmic TFLOP/s (4*d
+flops per visible (query, key) pair); the ``decode`` object carries the
+decode's algorithmic HBM GB/s (Q + latent KV + O + LSE bytes, each once).
+``roofline`` compares the prefill kernel with the bf16 MFMA peak;
+``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
+prefill workload on the host cores.
+
+Options: --gpus N (only 1 is supported), --steps K, --warmup W,
+--workloads a,b,... (default: causal_prefill_bf16,mla_decode_bf16; "all"
+adds the other configurations as extra lines in ``extra``),
+--no-cpu-baseline, --cpu-seconds S.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (prefill, % MFMA peak); decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PRIMARY = "causal_prefill_bf16"
+DECODE = "mla_decode_bf16"
+KERNEL_SOURCES = {
+    "fwd_bf16": "tiled_attention_amd/csrc/fwd_bf16.hip",
+    "fwd_f32": "tiled_attention_amd/csrc/fwd_f32.hip",
+    "decode_mla": "tiled_attention_amd/csrc/decode_mla.hip",
+}
+
+
+def visible_pairs(lens_q, lens_k, causal, window):
+    """Exact number of visible (query, key) pairs (bottom-right alignment, inclusive window)."""
+    total = 0
+    wl, wr = window
+    for sq, sk in zip(lens_q, lens_k):
+        if sq == 0 or sk == 0:
+            continue
+        pos = np.arange(sq, dtype=np.int64) + (sk - sq)
+        lo = np.zeros(sq, dtype=np.int64) if wl < 0 else np.maximum(0, pos - wl)
+        hi = np.full(sq, sk - 1, dtype=np.int64)
+        if causal:
+            hi = np.minimum(hi, pos)
+        if wr >= 0:
+            hi = np.minimum(hi, pos + wr)
+        total += int(np.maximum(0, hi - lo + 1).sum())
+    return total
+
+
+def work_of(w, inp):
+    """Algorithmic flops and bytes of one call on workload w."""
+    pairs = visible_pairs(inp["lens_q"], inp["lens_k"], w.causal, w.window) * w.heads_q
+    flops = pairs * 2 * (w.d_qk + w.d_v)
+    esz = 4 if w.dtype == "f32" else 2
+    tq, tk = sum(inp["lens_q"]), sum(inp["lens_k"])
+    q_b = tq * w.heads_q * w.d_qk * esz
+    o_b = tq * w.heads_q * w.d_v * esz
+    lse_b = tq * w.heads_q * 4
+    if w.kind == "decode":
+        kv_b = tk * w.heads_kv * w.d_qk * esz  # shared latent kv, read once
+    else:
+        kv_b = tk * w.heads_kv * (w.d_qk + w.d_v) * esz
+    return pairs, flops, q_b + kv_b + o_b + lse_b
+
+
+def source_sha(name):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[name]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM traffic per launch from committed rocprofv3 PMC runs, if taken on this exact source."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Runner:
+    """Inputs resident on the GPU plus a closure that launches one call."""
+
+    def __init__(self, name):
+        import torch
+
+        import tiled_attention_amd as mx
+        import workloads
+
+        self.w = w = workloads.get(name)
+        self.inp = inp = workloads.make_inputs(w)
+        dev = torch.device("cuda:0")
+        self.pairs, self.flops, self.bytes = work_of(w, inp)
+        scale = w.softmax_scale
+        if w.kind == "dense":
+            q, k, v = (inp[x].to(dev) for x in "qkv")
+            o = torch.empty_like(q)
+            lse = torch.empty((w.batch, w.heads_q, w.seqlen_q), dtype=torch.float32, device=dev)
+            self.call = lambda: mx.mxfa_fwd(q, k, v, causal=w.causal, window=w.window, softcap=w.softcap,
+                                            scale=scale, out=o, lse=lse)
+            self.kernel = "fwd_bf16" if w.dtype == "bf16" else "fwd_f32"
+        elif w.kind == "varlen":
+            q, k, v = (inp[x].to(dev) for x in "qkv")
+            cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
+            mq, mk = max(inp["lens_q"]), max(inp["lens_k"])
+            o = torch.empty_like(q)
+            lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device=dev)
+            self.call = lambda: mx.mxfa_fwd_varlen(q, k, v, cq, ck, mq, mk, causal=w.causal, window=w.window,
+                                                   softcap=w.softcap, scale=scale, out=o, lse=lse)
+            self.kernel = "fwd_bf16"
+        else:
+            q, kv = inp["q"].to(dev), inp["kv"].to(dev)
+            cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
+            o = torch.empty((q.shape[0], w.heads_q, w.d_v), dtype=q.dtype, device=dev)
+            lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device=dev)
+            self.splits = mx.mxfa_decode_splitkv_num_splits(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv)
+            nbytes = mx.mxfa_decode_splitkv_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q,
+                                                            w.heads_kv, w.d_v)
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+            self.call = lambda: mx.mxfa_decode_splitkv(q, kv, cq, ck, w.seqlen_q, w.seqlen_k, head_dim_v=w.d_v,
+                                                       scale=scale, workspace=ws, out=o, lse=lse)
+            self.kernel = "decode_mla"
+        torch.cuda.synchronize()
+
+    def time(self, steps, warmup):
+        import torch
+
+        for _ in range(warmup):
+            self.call()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            self.call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps  # ms per call
+
+
+def cpu_baseline(name, target_s):
+    """Time the fp64 oracle on a bounded, seeded sample of workload rows (host cores)."""
+    import oracle
+    import workloads
+
+    w = workloads.get(name)
+    inp = workloads.make_inputs(w)
+    to_np = workloads.to_numpy_bits
+    if w.kind == "dense":
+        q = to_np(inp["q"]).reshape(-1, w.heads_q, w.d_qk)
+        k = to_np(inp["k"]).reshape(-1, w.heads_kv, w.d_qk)
+        v = to_np(inp["v"]).reshape(-1, w.heads_kv, w.d_v)
+    elif w.kind == "varlen":
+        q, k, v = to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"])
+    else:
+        q = to_np(inp["q"])
+        k = to_np(inp["kv"])
+        v = k[:, :, :w.d_v]
+    cq, ck = inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy()
+    total_rows = q.shape[0] * w.heads_q
+    rng = np.random.RandomState(12345)
+    order = rng.permutation(total_rows)
+    tok_of = order // w.heads_q
+    head_of = order % w.heads_q
+    # per-row visible key counts for the flop count of the sample
+    starts = np.repeat(cq[:-1], np.diff(cq))
+    seg = np.repeat(np.arange(len(cq) - 1), np.diff(cq))
+    i = np.arange(q.shape[0]) - starts
+    sk = (ck[1:] - ck[:-1])[seg]
+    sq = (cq[1:] - cq[:-1])[seg]
+    pos = i + sk - sq
+    lo = np.zeros_like(pos) if w.window[0] < 0 else np.maximum(0, pos - w.window[0])
+    hi = sk - 1
+    if w.causal:
+        hi = np.minimum(hi, pos)
+    if w.window[1] >= 0:
+        hi = np.minimum(hi, pos + w.window[1])
+    cnt = np.maximum(0, hi - lo + 1)
+    threads = oracle.threads_used(0)
+    n = min(total_rows, 256)
+    done = 0
+    elapsed = 0.0
+    pairs = 0
+    while done < total_rows:
+        rows = np.stack([tok_of[done:done + n], head_of[done:done + n]], axis=1)
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, k, v, cq, ck, causal=w.causal, window=w.window, softcap=w.softcap,
+                              scale=w.softmax_scale, rows=rows)
+        elapsed += time.perf_counter() - t0
+        pairs += int(cnt[rows[:, 0]].sum())
+        done += n
+        if elapsed >= target_s:
+            break
+        rate = done / max(elapsed, 1e-9)
+        n = int(min(total_rows - done, max(256, rate * (target_s - elapsed))))
+    flops = pairs * 2 * (w.d_qk + w.d_v)
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of {total_rows} (token, head) rows of {name}, seeded random order; "
+                  f"{pairs} visible pairs in {elapsed:.1f} s",
+        "seconds": round(elapsed, 2),
+        "cpu_model": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default=f"{PRIMARY},{DECODE}")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the multi-GPU sharding is a design, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tiled_attention_amd as mx
+
+    mx.load_library()  # fails loudly when the HIP library is not built
+    names = args.workloads.split(",")
+    if names == ["all"]:
+        names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16"]
+    if PRIMARY not in names:
+        names.insert(0, PRIMARY)
+
+    results = {}
+    for name in names:
+        print(f"[bench] {name}: preparing inputs", file=sys.stderr, flush=True)
+        r = Runner(name)
+        ms = r.time(args.steps, args.warmup)
+        res = {
+            "workload": name,
+            "ms": round(ms, 4),
+            "tflops": r.flops / (ms * 1e-3) / 1e12,
+            "gbs": r.bytes / (ms * 1e-3) / 1e9,
+            "flops_per_call": r.flops,
+            "bytes_per_call": r.bytes,
+            "kernel": r.kernel,
+        }
+        if r.w.kind == "decode":
+            res["splits"] = r.splits
+        results[name] = res
+        print(f"[bench] {name}: {ms:.4f} ms/call, {res['tflops']:.1f} TFLOP/s, {res['gbs']:.1f} GB/s",
+              file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+    p = results[PRIMARY]
+    w = __import__("workloads").get(PRIMARY)
+    line = {
+        "metric": METRIC,
+        "value": round(p["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16 RNE)",
+        "config": {"workload": PRIMARY, "batch": w.batch, "seqlen": w.seqlen_q, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "head_dim": w.d_qk, "causal": w.causal, "parallelism": "single GPU"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(p["tflops"], 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(p["tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": load_traffic(p["kernel"]),
+            "kernel": p["kernel"],
+            "flops_per_launch": p["flops_per_call"],
+        },
+    }
+    if DECODE in results:
+        d = results[DECODE]
+        line["decode"] = {
+            "workload": DECODE,
+            "value": round(d["gbs"], 1),
+            "unit": "GB/s",
+            "ms": d["ms"],
+            "splits": d.get("splits"),
+            "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(d["gbs"] / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_mla"),
+                         "bytes_per_launch": d["bytes_per_call"],
+                         "note": "one call = split kernel + combine kernel"},
+        }
+    extra = [v for k, v in results.items() if k not in (PRIMARY, DECODE)]
+    if extra:
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline: fp64 oracle on a sample of the prefill workload", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(PRIMARY, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

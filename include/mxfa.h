@@ -1,0 +1,156 @@
+/*
+ * mxfa.h -- fused scaled-dot-product attention forward for MI355X (gfx950).
+ *
+ * C ABI of libmxfa.so. Every call computes, on the caller's HIP stream,
+ *
+ *     O = softmax(scale * Q K^T + mask) V        and      LSE = log sum exp(row scores)
+ *
+ * tile by tile with a running row max and sum, so the score matrix is never
+ * stored. The operation is the one stated by the mxflashattn 1.4.0 page
+ * (api.py: flash_attn_func / flash_attn_varlen_func; prefill.py:
+ * prefill_chunked_reference) and computed, tile by tile, as in the
+ * oxillama-runtime 0.1.0 page (src/flash_attention.rs, flash_attention).
+ *
+ * Semantics shared by every entry point
+ * -------------------------------------
+ *  - Row i of a segment with Sq queries and Sk keys sits at key position
+ *    pos = i + (Sk - Sq) (bottom-right alignment, as in prefill_chunked_reference).
+ *    Key j is visible iff 0 <= j < Sk, and j <= pos when causal, and
+ *    j >= pos - window_left when window_left >= 0, and j <= pos + window_right
+ *    when window_right >= 0 (window bounds inclusive; -1 = unbounded).
+ *  - Score of a visible key: t = scale * <q_i, k_j>; when softcap > 0 it is
+ *    replaced by softcap * tanh(t / softcap) before the softmax.
+ *  - Query head h reads key/value head h / (heads_q / heads_kv) (grouped-query
+ *    attention; flash_attention_gqa on the oxillama-runtime page).
+ *  - A row that sees no key gets O = 0 and LSE = -inf.
+ *  - LSE is float32, natural log.
+ *  - bf16 inputs: products accumulate in fp32; O is rounded to bf16 with
+ *    round-to-nearest-even. f32 inputs: fp32 throughout.
+ *
+ * Ownership and execution
+ * -----------------------
+ *  - All tensor pointers are device pointers owned by the caller; the library
+ *    keeps none of them after the call returns and allocates no device memory.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and is complete
+ *    when the stream reaches that point. No call synchronises the device.
+ *  - Tensors are contiguous in the layouts stated per call. q, k, v, kv and o
+ *    must be 16-byte aligned; lse and cu_seqlens 4-byte aligned.
+ *  - The contents of cu_seqlens (non-decreasing, starting at 0, last entry =
+ *    total) are the caller's contract and are not checked on the device.
+ *
+ * Errors
+ * ------
+ *  Every call returns an mxfa_status. Arguments are checked on the host
+ *  before anything is enqueued; on a non-OK status nothing was enqueued.
+ *  mxfa_last_error() returns a message for the calling thread's last non-OK
+ *  status. The library never aborts and never prints.
+ */
+#ifndef MXFA_H
+#define MXFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* mxfa_stream_t; /* the same handle as hipStream_t */
+
+typedef enum {
+    MXFA_OK = 0,
+    MXFA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent heads, ... */
+    MXFA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for */
+    MXFA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query says */
+    MXFA_ERR_HIP = 4          /* the HIP runtime reported an error (launch, device query) */
+} mxfa_status;
+
+typedef enum { MXFA_F32 = 0, MXFA_BF16 = 1 } mxfa_dtype;
+
+/*
+ * Dense forward (flash_attn_func on the mxflashattn page).
+ *   q   [batch, seqlen_q, heads_q,  head_dim]
+ *   k,v [batch, seqlen_k, heads_kv, head_dim]
+ *   o   [batch, seqlen_q, heads_q,  head_dim]     (written)
+ *   lse [batch, heads_q, seqlen_q] float32       (written; may be NULL)
+ * dtype: MXFA_F32 or MXFA_BF16 for q, k, v and o alike. head_dim: 64 or 128.
+ * batch, seqlen_q, seqlen_k >= 0 (zero-sized calls return MXFA_OK).
+ * heads_kv >= 1 divides heads_q. window_left/right >= -1. softcap >= 0 and
+ * finite (0 = off). scale finite.
+ */
+mxfa_status mxfa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int batch, int seqlen_q, int seqlen_k, int heads_q, int heads_kv,
+                     int head_dim, mxfa_dtype dtype, int causal, int window_left,
+                     int window_right, float softcap, float scale, mxfa_stream_t stream);
+
+/*
+ * Packed variable-length forward (flash_attn_varlen_func on the mxflashattn
+ * page; packed batches as in the lattice-inference page's
+ * src/attention/standard.rs). Segment b owns query tokens
+ * [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key tokens
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); segments never attend to each other.
+ *   q   [total_q, heads_q,  head_dim]      k, v [total_k, heads_kv, head_dim]
+ *   o   [total_q, heads_q,  head_dim]      lse  [heads_q, total_q] float32 (may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k: int32 device arrays of batch + 1 entries.
+ * max_seqlen_q / max_seqlen_k must bound every segment's length (they size the
+ * launch; a segment longer than max_seqlen_q is not fully computed).
+ * Other arguments as for mxfa_fwd.
+ */
+mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                            int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                            int heads_q, int heads_kv, int head_dim, mxfa_dtype dtype, int causal,
+                            int window_left, int window_right, float softcap, float scale,
+                            mxfa_stream_t stream);
+
+/*
+ * Split-KV decode over a shared latent KV (the kernelbot amd-mixed-mla
+ * submission 588924 page: _flash_splitk then _reduce_splitk; the split /
+ * combine scheme of the AstrAI v1.3.9 page's attn_decode_split_kv_mma.cuh).
+ * The keys are the full kv rows; the values are their first head_dim_v
+ * channels. Each split of the key range writes an un-normalised partial
+ * (acc, row max, row sum) into the workspace; a combine kernel merges them.
+ *   q   [total_q, heads_q,  head_dim_qk] bf16    kv [total_k, heads_kv, head_dim_qk] bf16
+ *   o   [total_q, heads_q,  head_dim_v]  bf16    lse [heads_q, total_q] float32 (may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k as for mxfa_fwd_varlen.
+ * Supported: head_dim_qk = 576, head_dim_v = 512, bf16.
+ * num_splits: 0 picks a split count from the device's compute-unit count;
+ * otherwise 1..64 (the result does not depend on it beyond fp32 rounding).
+ * workspace: device memory of at least mxfa_decode_splitkv_workspace_bytes()
+ * bytes with the same batch/max_seqlen_q/heads/num_splits arguments; owned by
+ * the caller, overwritten, not needed after the stream passes the call.
+ * Other arguments as for mxfa_fwd.
+ */
+mxfa_status mxfa_decode_splitkv(const void* q, const void* kv, void* o, float* lse,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                                int total_k, int heads_q, int heads_kv, int head_dim_qk,
+                                int head_dim_v, int causal, int window_left, int window_right,
+                                float softcap, float scale, int num_splits, void* workspace,
+                                size_t workspace_bytes, mxfa_stream_t stream);
+
+/*
+ * Workspace bytes mxfa_decode_splitkv needs for these arguments (0 when
+ * nothing is needed). With num_splits = 0 it queries the current device's
+ * compute-unit count (a host-side HIP query, no device work); if that fails
+ * it returns 0 and sets mxfa_last_error().
+ */
+size_t mxfa_decode_splitkv_workspace_bytes(int batch, int max_seqlen_q, int max_seqlen_k,
+                                           int heads_q, int heads_kv, int head_dim_v,
+                                           int num_splits);
+
+/* Split count mxfa_decode_splitkv uses for these arguments (0 on error). */
+int mxfa_decode_splitkv_num_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q,
+                                   int heads_kv, int num_splits);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* mxfa_last_error(void);
+
+/* Library version string, e.g. "mxfa 0.1.0 gfx950". */
+const char* mxfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFA_H */

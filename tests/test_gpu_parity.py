@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small problems compare every element; they span several q/k tiles with ragged
+tails, GQA, Sq != Sk (bottom-right causal), fully-masked rows, empty
+segments, windows and softcap. The five headline workloads run at full size
+in the launch configuration the bench times, compared on seeded sampled rows
+(every segment's first/last rows and q-tile edges included). Tolerances:
+max |O - O_ref| <= 1e-5 (fp32) or 1e-2 (bf16), |LSE - LSE_ref| <= 1e-4.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_helpers import compare, dev, gpu_varlen, oracle_varlen, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("tiled_attention_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mx.load_library()
+
+
+# (dtype, d, batch, sq, sk, hq, hkv, causal, window, softcap)
+DENSE_CASES = [
+    ("bf16", 128, 2, 1, 1, 2, 1, True, (-1, -1), 0.0),
+    ("bf16", 128, 2, 15, 15, 4, 2, True, (-1, -1), 0.0),
+    ("bf16", 128, 1, 129, 129, 8, 2, True, (-1, -1), 0.0),
+    ("bf16", 128, 2, 300, 300, 4, 4, False, (-1, -1), 0.0),
+    ("bf16", 64, 2, 65, 65, 4, 1, True, (-1, -1), 0.0),
+    ("bf16", 64, 1, 127, 200, 2, 1, True, (-1, -1), 0.0),
+    ("bf16", 128, 1, 200, 90, 2, 2, True, (-1, -1), 0.0),
+    ("bf16", 128, 1, 333, 333, 4, 2, True, (50, 0), 0.0),
+    ("bf16", 128, 1, 257, 257, 4, 1, True, (64, 0), 50.0),
+    ("bf16", 128, 1, 190, 190, 2, 2, False, (17, 9), 0.0),
+    ("bf16", 128, 1, 100, 100, 2, 1, False, (-1, -1), 5.0),
+    ("bf16", 64, 3, 96, 160, 6, 3, False, (-1, 40), 0.0),
+    ("f32", 64, 1, 128, 128, 1, 1, False, (-1, -1), 0.0),
+    ("f32", 128, 2, 70, 70, 4, 2, True, (20, 0), 30.0),
+    ("f32", 64, 1, 33, 80, 2, 1, True, (-1, -1), 0.0),
+    ("f32", 64, 2, 100, 100, 2, 2, False, (5, 5), 0.0),
+]
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=[
+    f"{c[0]}-d{c[1]}-b{c[2]}-{c[3]}x{c[4]}-h{c[5]}/{c[6]}-c{int(c[7])}-w{c[8][0]},{c[8][1]}-cap{c[9]:g}"
+    for c in DENSE_CASES])
+def test_dense_matches_oracle(case):
+    dtype, d, b, sq, sk, hq, hkv, causal, window, cap = case
+    seed = 1000 + DENSE_CASES.index(case)
+    print(f"[dense] {case} seed={seed}", flush=True)
+    p = workloads.make_problem(seed, dtype=dtype, heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d,
+                               lens_q=[sq] * b, lens_k=[sk] * b, dense=True)
+    scale = d ** -0.5
+    q, k, v = p["q"].to(dev()), p["k"].to(dev()), p["v"].to(dev())
+    o, lse = mx.mxfa_fwd(q, k, v, causal=causal, window=window, softcap=cap, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, _ = oracle_varlen(
+        {"q": p["q"].reshape(b * sq, hq, d), "k": p["k"].reshape(b * sk, hkv, d),
+         "v": p["v"].reshape(b * sk, hkv, d), "cu_seqlens_q": p["cu_seqlens_q"], "cu_seqlens_k": p["cu_seqlens_k"]},
+        causal=causal, window=window, softcap=cap, scale=scale)
+    o_g = o.float().cpu().numpy().reshape(b * sq * hq, d)
+    lse_g = lse.cpu().numpy().transpose(0, 2, 1).reshape(-1)  # [B,Hq,Sq] -> token-major rows
+    compare(o_g, lse_g, o_ref.reshape(-1, d), lse_ref.reshape(-1), dtype, str(case))
+
+
+# (dtype, d, lens_q, lens_k, hq, hkv, causal, window, softcap)
+VARLEN_CASES = [
+    ("bf16", 128, [1, 0, 130, 64, 257], [1, 0, 130, 64, 257], 4, 2, True, (-1, -1), 0.0),
+    ("bf16", 128, [50, 200, 7], [90, 200, 300], 8, 2, True, (-1, -1), 0.0),
+    ("bf16", 64, [3, 129, 0, 65], [0, 129, 10, 80], 2, 1, True, (30, 0), 0.0),
+    ("bf16", 128, [140, 33], [140, 33], 4, 1, True, (100, 0), 50.0),
+    ("bf16", 128, [77, 250], [77, 250], 2, 2, False, (-1, -1), 0.0),
+    ("f32", 64, [10, 0, 70], [10, 5, 70], 4, 4, True, (-1, -1), 0.0),
+    ("f32", 128, [65, 31], [65, 40], 2, 1, False, (8, 3), 20.0),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=[f"varlen{i}" for i in range(len(VARLEN_CASES))])
+def test_varlen_matches_oracle(case):
+    dtype, d, lq, lk, hq, hkv, causal, window, cap = case
+    seed = 2000 + VARLEN_CASES.index(case)
+    print(f"[varlen] {case} seed={seed}", flush=True)
+    p = workloads.make_problem(seed, dtype=dtype, heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=lq, lens_k=lk)
+    scale = d ** -0.5
+    o_g, lse_g = gpu_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
+    o_ref, lse_ref, _ = oracle_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
+    compare(o_g.reshape(-1, d), lse_g.T.reshape(-1), o_ref.reshape(-1, d), lse_ref.reshape(-1), dtype, str(case))
+
+
+def test_zero_length_calls_are_noops():
+    q = torch.empty((0, 16, 4, 128), dtype=torch.bfloat16, device=dev())
+    o, lse = mx.mxfa_fwd(q, q, q)
+    assert o.numel() == 0
+    k = torch.empty((2, 0, 4, 128), dtype=torch.bfloat16, device=dev())
+    q = torch.randn((2, 5, 4, 128), device=dev()).bfloat16()
+    o, lse = mx.mxfa_fwd(q, k, k)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_first_causal_row_is_v0_exactly():
+    p = workloads.make_problem(7, dtype="bf16", heads_q=4, heads_kv=2, d_qk=128, d_v=128, lens_q=[300] * 2,
+                               lens_k=[300] * 2, dense=True)
+    q, k, v = (p[x].to(dev()) for x in "qkv")
+    o, _ = mx.mxfa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    for h in range(4):
+        assert torch.equal(o[:, 0, h].cpu(), p["v"][:, 0, h // 2])
+
+
+def test_zero_query_lse_counts_keys():
+    """q = 0: LSE = ln(number of visible keys) at every row, window (64, 0) causal + Sq < Sk."""
+    p = workloads.make_problem(8, dtype="bf16", heads_q=2, heads_kv=1, d_qk=128, d_v=128, lens_q=[300],
+                               lens_k=[350], dense=True)
+    q = torch.zeros_like(p["q"]).to(dev())
+    k, v = p["k"].to(dev()), p["v"].to(dev())
+    _, lse = mx.mxfa_fwd(q, k, v, causal=True, window=(64, 0))
+    torch.cuda.synchronize()
+    lse = lse.cpu().double()
+    for i in range(300):
+        pos = i + 50
+        cnt = min(pos, 64) + 1
+        assert abs(lse[0, 0, i].item() - math.log(cnt)) < 1e-4
+
+
+def test_gqa_equals_mha_bitwise():
+    p = workloads.make_problem(9, dtype="bf16", heads_q=8, heads_kv=2, d_qk=128, d_v=128, lens_q=[200] * 2,
+                               lens_k=[200] * 2, dense=True)
+    q, k, v = (p[x].to(dev()) for x in "qkv")
+    o1, l1 = mx.mxfa_fwd(q, k, v, causal=True)
+    o2, l2 = mx.mxfa_fwd(q, k.repeat_interleave(4, dim=2).contiguous(), v.repeat_interleave(4, dim=2).contiguous(),
+                         causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_varlen_equals_per_segment_bitwise():
+    lens = [100, 257, 1, 64]
+    p = workloads.make_problem(10, dtype="bf16", heads_q=4, heads_kv=2, d_qk=128, d_v=128, lens_q=lens, lens_k=lens)
+    d = dev()
+    q, k, v = p["q"].to(d), p["k"].to(d), p["v"].to(d)
+    o, lse = mx.mxfa_fwd_varlen(q, k, v, p["cu_seqlens_q"].to(d), p["cu_seqlens_k"].to(d), max(lens), max(lens),
+                                causal=True)
+    start = 0
+    for L in lens:
+        ob, lb = mx.mxfa_fwd(q[start:start + L][None].contiguous(), k[start:start + L][None].contiguous(),
+                             v[start:start + L][None].contiguous(), causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o[start:start + L], ob[0])
+        assert torch.equal(lse[:, start:start + L], lb[0])
+        start += L
+
+
+def test_deterministic_bitwise():
+    w = workloads.get("causal_prefill_bf16", batch=1, heads_q=4, heads_kv=4, seqlen_q=1000, seqlen_k=1000)
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[x].to(dev()) for x in "qkv")
+    o1, l1 = mx.mxfa_fwd(q, k, v, causal=True)
+    o2, l2 = mx.mxfa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ decode
+
+# (lens_q, lens_k, hq, hkv, causal, window, softcap, splits)
+DECODE_CASES = [
+    ([1, 4, 2], [1, 70, 300], 16, 1, False, (-1, -1), 0.0, 0),
+    ([4, 4], [1000, 129], 16, 1, False, (-1, -1), 0.0, 3),
+    ([9, 1], [200, 64], 16, 2, False, (-1, -1), 0.0, 2),
+    ([4, 3], [500, 65], 16, 1, True, (-1, -1), 0.0, 4),
+    ([4], [700], 16, 1, True, (100, 0), 30.0, 5),
+    ([2, 0, 5], [64, 10, 0], 8, 1, False, (-1, -1), 0.0, 1),
+]
+
+
+def _run_decode(p, hq, causal, window, cap, splits, scale):
+    d = dev()
+    q, kv = p["q"].to(d), p["kv"].to(d)
+    cq, ck = p["cu_seqlens_q"].to(d), p["cu_seqlens_k"].to(d)
+    o, lse = mx.mxfa_decode_splitkv(q, kv, cq, ck, max(p["lens_q"]), max(p["lens_k"]), head_dim_v=512,
+                                    causal=causal, window=window, softcap=cap, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[f"decode{i}" for i in range(len(DECODE_CASES))])
+def test_decode_matches_oracle(case):
+    lq, lk, hq, hkv, causal, window, cap, splits = case
+    seed = 3000 + DECODE_CASES.index(case)
+    print(f"[decode] {case} seed={seed}", flush=True)
+    p = workloads.make_problem(seed, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    scale = 1.0 / math.sqrt(576)
+    o_g, lse_g = _run_decode(p, hq, causal, window, cap, splits, scale)
+    kv = to_np(p["kv"])
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kv, kv[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), causal=causal, window=window,
+                                              softcap=cap, scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            str(case))
+
+
+def test_decode_independent_of_split_count():
+    p = workloads.make_problem(3100, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=[4, 4, 1],
+                               lens_k=[2000, 333, 64], shared_kv=True)
+    scale = 1.0 / math.sqrt(576)
+    ref_o, ref_l = _run_decode(p, 16, False, (-1, -1), 0.0, 1, scale)
+    for s in (2, 3, 4, 8, 32):
+        o, l = _run_decode(p, 16, False, (-1, -1), 0.0, s, scale)
+        assert np.abs(o - ref_o).max() <= 1e-2
+        assert np.abs(l - ref_l).max() <= 1e-4
+    o2, l2 = _run_decode(p, 16, False, (-1, -1), 0.0, 4, scale)
+    o3, l3 = _run_decode(p, 16, False, (-1, -1), 0.0, 4, scale)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
+# --------------------------------------------------- headline workloads, full size
+
+def _full_dense_or_varlen(name, n_rows):
+    w = workloads.get(name)
+    print(f"[full] {name}: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    d = dev()
+    scale = w.softmax_scale
+    if w.kind == "dense":
+        q, k, v = (inp[x].to(d) for x in "qkv")
+        o, lse = mx.mxfa_fwd(q, k, v, causal=w.causal, window=w.window, softcap=w.softcap, scale=scale)
+        torch.cuda.synchronize()
+        o = o.reshape(-1, w.heads_q, w.d_v)
+        lse = lse.permute(0, 2, 1).reshape(-1, w.heads_q)  # token-major
+        qn = inp["q"].reshape(-1, w.heads_q, w.d_qk)
+        kn = inp["k"].reshape(-1, w.heads_kv, w.d_qk)
+        vn = inp["v"].reshape(-1, w.heads_kv, w.d_v)
+    else:
+        q, k, v = (inp[x].to(d) for x in "qkv")
+        o, lse = mx.mxfa_fwd_varlen(q, k, v, inp["cu_seqlens_q"].to(d), inp["cu_seqlens_k"].to(d),
+                                    max(inp["lens_q"]), max(inp["lens_k"]), causal=w.causal, window=w.window,
+                                    softcap=w.softcap, scale=scale)
+        torch.cuda.synchronize()
+        lse = lse.T
+        qn, kn, vn = inp["q"], inp["k"], inp["v"]
+    rows = sample_rows(inp["lens_q"], w.heads_q, n_rows, seed=w.seed)
+    print(f"[full] {name}: oracle on {len(rows)} rows", flush=True)
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(qn), to_np(kn), to_np(vn), inp["cu_seqlens_q"].numpy(),
+                                              inp["cu_seqlens_k"].numpy(), causal=w.causal, window=w.window,
+                                              softcap=w.softcap, scale=scale, rows=rows)
+    o_c = o.float().cpu().numpy()
+    lse_c = lse.cpu().numpy()
+    assert np.all(np.isfinite(lse_c)), "every row of these workloads sees at least one key"
+    got_o = o_c[rows[:, 0], rows[:, 1]]
+    got_l = lse_c[rows[:, 0], rows[:, 1]]
+    return compare(got_o, got_l, o_ref, lse_ref, w.dtype, name)
+
+
+def test_full_single_head_f32():
+    w = workloads.get("single_head_f32")
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[x].to(dev()) for x in "qkv")
+    o, lse = mx.mxfa_fwd(q, k, v, causal=False, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_dense(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]),
+                                               scale=w.softmax_scale)
+    compare(o.cpu().numpy().reshape(-1, 64), lse.cpu().numpy().transpose(0, 2, 1).reshape(-1),
+            o_ref.reshape(-1, 64), lse_ref.transpose(0, 2, 1).reshape(-1), "f32", "single_head_f32")
+
+
+def test_full_causal_prefill_bf16():
+    _full_dense_or_varlen("causal_prefill_bf16", 512)
+
+
+def test_full_varlen_gqa_causal_bf16():
+    _full_dense_or_varlen("varlen_gqa_causal_bf16", 512)
+
+
+def test_full_window_softcap_bf16():
+    _full_dense_or_varlen("window_softcap_bf16", 384)
+
+
+def test_full_mla_decode_bf16():
+    w = workloads.get("mla_decode_bf16")
+    print("[full] mla_decode_bf16: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    d = dev()
+    q, kv = inp["q"].to(d), inp["kv"].to(d)
+    o, lse = mx.mxfa_decode_splitkv(q, kv, inp["cu_seqlens_q"].to(d), inp["cu_seqlens_k"].to(d), w.seqlen_q,
+                                    w.seqlen_k, head_dim_v=w.d_v, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp["lens_q"], w.heads_q, 256, seed=w.seed)
+    import oracle
+
+    kvn = to_np(inp["kv"])
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(inp["q"]), kvn, kvn[:, :, :w.d_v], inp["cu_seqlens_q"].numpy(),
+                                              inp["cu_seqlens_k"].numpy(), scale=w.softmax_scale, rows=rows)
+    o_c = o.float().cpu().numpy()
+    lse_c = lse.T.cpu().numpy()
+    compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "mla_decode_bf16")

@@ -1,0 +1,123 @@
+// mxfa_device.h -- gfx950 device helpers: vector types, bf16 packing, MFMA
+// wrappers, exp2 and the mask / softcap transforms shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxfa_internal.h"
+
+namespace mxfa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+
+#define MXFA_DEV __device__ __forceinline__
+
+// ---------------------------------------------------------------- conversions
+
+// Two fp32 -> packed bf16x2 (round to nearest even; v_cvt_pk_bf16_f32).
+MXFA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(f, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+MXFA_DEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------- math
+
+// 2^x on the hardware transcendental unit (v_exp_f32); exp2(-inf) = 0.
+MXFA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+MXFA_DEV float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+MXFA_DEV float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Raw score s (= <q, k>) -> logit in log2 units (score * log2 e), with the
+// optional softcap applied to the scaled score:
+//   no cap: x = s * scale * log2e
+//   cap c : x = c * log2e * tanh(s * scale / c), tanh(y) = 1 - 2 / (exp(2y) + 1)
+template <bool kCap>
+MXFA_DEV float score_to_logit(float s, float x_mul, float cap_mul, float cap_out) {
+    if constexpr (kCap) {
+        const float e = fast_exp2(s * cap_mul);
+        return cap_out - 2.0f * cap_out * fast_rcp(e + 1.0f);
+    } else {
+        return s * x_mul;
+    }
+}
+
+// ---------------------------------------------------------------- visibility
+
+// Key j is visible to the query at key position pos (bottom-right aligned)
+// iff 0 <= j < sk, j <= pos (causal), pos - wl <= j (wl >= 0), j <= pos + wr (wr >= 0).
+struct KeyRange {
+    int lo;  // first visible key (inclusive)
+    int hi;  // last visible key (inclusive); hi < lo: no key
+};
+
+MXFA_DEV KeyRange visible_range(int pos, int sk, int causal, int wl, int wr) {
+    KeyRange r;
+    r.lo = 0;
+    r.hi = sk - 1;
+    if (causal) r.hi = min(r.hi, pos);
+    if (wr >= 0) r.hi = min(r.hi, pos + wr);
+    if (wl >= 0) r.lo = max(r.lo, pos - wl);
+    return r;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+// D = A * B + C for a 32x32 tile with a 16-deep contraction, bf16 inputs,
+// fp32 accumulate. Lane l holds A row (l % 32) and B column (l % 32), eight
+// contraction elements each (the same eight for A and B); D in the 32x32
+// accumulator layout: lane l, register r -> column l % 32,
+// row 8 * (r / 4) + 4 * (l / 32) + r % 4.
+MXFA_DEV f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- memory
+
+MXFA_DEV u32x4_t load_u32x4(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+MXFA_DEV void store_u32x4(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
+MXFA_DEV void store_u32x2(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
+
+// ---------------------------------------------------------------- work mapping
+
+// Workgroup -> (batch*head unit, q tile), longest work first, XCD aware.
+// Workgroups are handed to the 8 XCDs round-robin by linear id, so id i runs
+// on XCD i % 8. Each XCD owns a contiguous range of (batch, head) units -- the
+// query heads of one kv head are adjacent, so they share K/V in that XCD's
+// L2 -- and walks its units' q tiles from the last (most keys under a causal
+// mask) to the first.
+struct WorkItem {
+    int unit;   // b * heads_q + h, or -1 for a padding workgroup
+    int qtile;
+};
+
+MXFA_DEV WorkItem map_workgroup(int id, int units, int units_per_xcd, int n_qtiles) {
+    const int x = id % kXcds;
+    const int n = id / kXcds;
+    const int u0 = (int)(((long long)x * units) / kXcds);
+    const int u1 = (int)(((long long)(x + 1) * units) / kXcds);
+    const int rank = n / units_per_xcd;
+    const int j = n % units_per_xcd;
+    WorkItem w;
+    w.unit = (u0 + j < u1 && rank < n_qtiles) ? u0 + j : -1;
+    w.qtile = n_qtiles - 1 - rank;
+    return w;
+}
+
+}  // namespace mxfa

@@ -1,0 +1,76 @@
+// mxfa_internal.h -- kernel parameter blocks and launcher declarations shared
+// by the C-ABI layer (mxfa_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfa {
+
+// One forward problem (dense or packed). Dense problems leave cu_q/cu_k null
+// and use seqlen_q/seqlen_k for every segment; packed problems read the
+// segment bounds from cu_q/cu_k and use seqlen_q/seqlen_k as upper bounds.
+struct FwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;              // may be null
+    const int32_t* cu_q;     // null for dense
+    const int32_t* cu_k;
+    int batch;
+    int seqlen_q;            // dense: every segment; packed: max over segments
+    int seqlen_k;
+    int total_q;             // packed LSE row stride ([Hq, total_q])
+    int heads_q;
+    int heads_kv;
+    int group;               // heads_q / heads_kv
+    int causal;
+    int window_left;         // -1 = unbounded
+    int window_right;
+    float softcap;           // 0 = off
+    float scale;             // softmax scale
+    float x_mul;             // score -> log2-domain logit multiplier (no cap: scale*log2e)
+    float cap_mul;           // cap: 2*log2e*scale/cap
+    float cap_out;           // cap: cap*log2e
+    int n_qtiles;            // ceil(seqlen_q / BM)
+    int units;               // batch * heads_q
+    int units_per_xcd;       // ceil(units / 8)
+};
+
+// One latent-KV split decode.
+struct DecodeParams {
+    const void* q;
+    const void* kv;
+    void* o;
+    float* lse;              // may be null
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    float* part_acc;         // [batch, m_groups, splits, 64, d_v] fp32
+    float* part_ml;          // [batch, m_groups, splits, 2, 64] fp32 (max, sum)
+    int batch;
+    int max_seqlen_q;
+    int max_seqlen_k;
+    int total_q;
+    int heads_q;
+    int heads_kv;
+    int group;
+    int m_groups;            // ceil(max_seqlen_q * group / 64)
+    int splits;
+    int causal;
+    int window_left;
+    int window_right;
+    float softcap;
+    float x_mul;
+    float cap_mul;
+    float cap_out;
+};
+
+hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+
+// Rows of one decode work group: (query token, head-in-group) pairs.
+constexpr int kDecodeRows = 64;
+
+}  // namespace mxfa
