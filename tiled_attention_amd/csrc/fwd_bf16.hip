@@ -3,38 +3,86 @@
 // Tiled online-softmax forward as on the oxillama-runtime 0.1.0 page
 // (src/flash_attention.rs, flash_attention: running row max, running sum,
 // rescale of the accumulator, final normalisation), in the exp2 domain with
-// the scale folded into one multiply after the QK^T contraction (kernelbot
+// the scale folded into the exponent after the QK^T contraction (kernelbot
 // amd-mixed-mla submission 588924, _flash_fused; scale applied in fp32 after
 // the MMA as in the AstrAI v1.3.9 page's attn_mma_utils.cuh), with causal and
 // window tiles skipped at tile granularity (flash_attention's causal tile skip,
 // extended to the window's lower edge).
 //
-// Work group: 4 waves, 128 query rows (32 per wave), one (batch, head) unit.
-// Each wave computes S^T = K Q^T for a 64-key tile with
+// Work group: 4 waves, 128 query rows (32 per wave), one (batch, head) unit,
+// two work groups per CU (<= 256 registers per lane, 64 KB LDS each).
+//
+// Per 64-key tile, each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, so lane l owns query row l % 32 and 32 of the 64
-// keys: the row max and row sum are in-register reductions plus one exchange
-// between the two lane halves. P^T stays in registers as the B operand of
-// O^T = V^T P^T (the accumulator layout of S^T is the operand layout of P^T),
-// and O^T keeps one query per lane so the online-softmax rescale is one
-// multiplier per lane.
+// keys: row max and row sum are in-register reductions plus one exchange
+// between the lane halves. P^T stays in registers as the B operand of
+// O^T = V^T P^T (the accumulator layout of S^T is the operand layout of
+// P^T); the V^T operand comes from LDS through ds_read_b64_tr_b16. O^T keeps
+// one query per lane, so the online-softmax rescale is one multiplier per
+// lane, and it is skipped unless some row's max grew by more than 2^8.
+//
+// K/V tiles are double-buffered in LDS and filled by buffer loads that write
+// LDS directly (out-of-range keys read as zero); the 16-byte chunks of a row
+// are XOR-swizzled so that the K operand reads (16 rows x one chunk) and the
+// transposing V reads (4 rows x 4 chunks per half wave) hit distinct banks.
 #include "mxfa_device.h"
 
 namespace mxfa {
 namespace {
 
-constexpr int BM = 128;       // query rows per work group
-constexpr int BN = 64;        // keys per tile
-constexpr int NTHREADS = 256; // 4 waves
+constexpr int BM = 128;        // query rows per work group
+constexpr int BN = 64;         // keys per tile
+constexpr int NTHREADS = 256;  // 4 waves
+constexpr float kLazyRescale = 8.0f;  // log2 units: rescale when a row max grows by > 2^8
 
-template <int D, bool kCap>
-__global__ __launch_bounds__(NTHREADS) void fwd_bf16_kernel(const FwdParams p) {
-    static_assert(D % 32 == 0, "head dim must be a multiple of 32");
-    constexpr int KSTEPS = D / 16;  // QK^T contraction steps
-    constexpr int DBLK = D / 32;    // 32-wide output blocks
-    constexpr int CPR = D / 8;      // 16-byte chunks per K/V row
+// Chunk swizzle of an LDS row (16-byte chunks): physical = logical ^ swz(row).
+template <int D>
+MXFA_DEV int swz(int row);
+template <>
+MXFA_DEV int swz<128>(int row) {  // 16 chunks per row, one row per 256-byte bank line
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+}
+template <>
+MXFA_DEV int swz<64>(int row) {  // 8 chunks per row, two rows per bank line
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[BN * D];
+// One 16-key step of O^T += V^T P^T: the V^T operands of all output blocks
+// (two transposing reads each) and one MFMA per 32-channel block.
+template <int D, int KB, int HALF>
+MXFA_DEV void pv_step(f32x16_t (&acc)[D / 32], const uint32_t (&pk)[2][8], const uint32_t (&va)[2 * (D / 32)]) {
+    constexpr int DBLK = D / 32;
+    constexpr int OFF = (KB * 32 + HALF * 16) * D * 2;
+    const u32x4_t pv = {pk[KB][HALF * 4 + 0], pk[KB][HALF * 4 + 1], pk[KB][HALF * 4 + 2], pk[KB][HALF * 4 + 3]};
+    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+    u32x2_t r[2 * DBLK];
+    if constexpr (DBLK == 4)
+        lds_read_tr16_x8<OFF>(r, va);
+    else
+        lds_read_tr16_x4<OFF>(r, va);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) {
+        const u32x4_t av = {r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+        acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pb, acc[db]);
+    }
+}
+
+// kMode 0: no softcap, scale > 0 -- the max runs on raw scores and the scale
+//          is folded into the exponent's FMA.
+// kMode 1: no softcap, any scale -- logits computed explicitly.
+// kMode 2: softcap.
+template <int D, int kMode>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_bf16_kernel(const FwdParams p) {
+    static_assert(D == 64 || D == 128, "head dim 64 or 128");
+    constexpr int KSTEPS = D / 16;             // QK^T contraction steps
+    constexpr int DBLK = D / 32;               // 32-wide output blocks
+    constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+    constexpr int ROWB = D * 2;                // bytes per K/V row in LDS
+    constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
+    constexpr int LOADS = TILEB / (16 * NTHREADS);  // 16-byte loads per thread per tile
+
+    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];  // [buffer][K, V]
 
     const WorkItem item = map_workgroup(blockIdx.x, p.units, p.units_per_xcd, p.n_qtiles);
     if (item.unit < 0) return;
@@ -65,11 +113,7 @@ __global__ __launch_bounds__(NTHREADS) void fwd_bf16_kernel(const FwdParams p) {
     const long long q_tok = (long long)p.heads_q * D;
     const long long kv_tok = (long long)p.heads_kv * D;
 
-    const uint16_t* __restrict__ Q = static_cast<const uint16_t*>(p.q);
-    const uint16_t* __restrict__ K = static_cast<const uint16_t*>(p.k);
-    const uint16_t* __restrict__ V = static_cast<const uint16_t*>(p.v);
-
-    // Key range of the whole group: lo/hi of a row are non-decreasing in the row.
+    // Key range of the whole group (lo/hi of a row are non-decreasing in the row).
     const int row_last = min(tile_row0 + BM, sq) - 1;
     const int kv_lo = visible_range(tile_row0 + off, sk, p.causal, p.window_left, p.window_right).lo;
     const int kv_hi = visible_range(row_last + off, sk, p.causal, p.window_left, p.window_right).hi;
@@ -89,7 +133,8 @@ __global__ __launch_bounds__(NTHREADS) void fwd_bf16_kernel(const FwdParams p) {
     // Q^T as the B operand: lane holds row qi, contraction chunk ks*16 + lh*8.
     bf16x8_t qreg[KSTEPS];
     {
-        const uint16_t* qp = Q + (long long)(q_start + qi) * q_tok + (long long)h * D + lh * 8;
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (long long)(q_start + qi) * q_tok +
+                             (long long)h * D + lh * 8;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4_t v = {0u, 0u, 0u, 0u};
@@ -98,110 +143,145 @@ __global__ __launch_bounds__(NTHREADS) void fwd_bf16_kernel(const FwdParams p) {
         }
     }
 
+    // LDS read offsets (bytes within a tile). K operand: row kb*32 + lr, chunk ks*2 + lh.
+    const int f_lr = swz<D>(lr & 15);
+    int koff[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = lr * ROWB + (((ks * 2 + lh) ^ f_lr) << 4);
+    // V^T operand via transposing reads: 16-lane group g, lane i reads row
+    // (which*8 + 4*(g/2) + i/4) of a 16-key step, columns db*32 + (g%2)*16 + 4*(i%4).
+    int voff[2][DBLK];
+    {
+        const int g = lane >> 4;
+        const int i = lane & 15;
+        const int cl = (g & 1) * 2 + ((i & 3) >> 1);
+#pragma unroll
+        for (int which = 0; which < 2; ++which) {
+            const int rowl = which * 8 + 4 * (g >> 1) + (i >> 2);
+            const int fw = swz<D>(rowl);
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+                voff[which][db] = rowl * ROWB + (((db * 4 + cl) ^ fw) << 4) + (i & 1) * 8;
+        }
+    }
+    // Global -> LDS loads: 16-byte chunk position P = n*256 + tid of a tile.
+    uint32_t goff[LOADS];
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+        const int P = n * NTHREADS + tid;
+        const int row = P / CPR;
+        const int c = (P % CPR) ^ swz<D>(row & 15);
+        goff[n] = (uint32_t)(((long long)row * kv_tok + c * 8) * 2);
+    }
+    const uint16_t* Kseg = static_cast<const uint16_t*>(p.k) + (long long)k_start * kv_tok + (long long)kvh * D;
+    const uint16_t* Vseg = static_cast<const uint16_t*>(p.v) + (long long)k_start * kv_tok + (long long)kvh * D;
+
+    auto issue_tile = [&](int kt, int buf) {
+        // Bytes of the tile that hold keys < sk (keys past the end read as zero).
+        long long bytes = (long long)(sk - kt - 1) * kv_tok * 2 + D * 2;
+        if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kseg + (long long)kt * kv_tok, (uint32_t)bytes);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vseg + (long long)kt * kv_tok, (uint32_t)bytes);
+#pragma unroll
+        for (int n = 0; n < LOADS; ++n) {
+            buffer_load_lds16(rk, &smem[buf][0][(n * NTHREADS + wave * 64) * 16], goff[n]);
+            buffer_load_lds16(rv, &smem[buf][1][(n * NTHREADS + wave * 64) * 16], goff[n]);
+        }
+    };
+
     f32x16_t acc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) acc[i] = f32x16_t{};
-    float m_run = -INFINITY;  // running max of this row, log2 units
+    float m_run = -INFINITY;  // running max of this row, log2 units (may trail the true max by <= 8)
     float l_part = 0.0f;      // running sum over this lane's keys
+    const float c_exp = (kMode == 0) ? p.x_mul : 1.0f;
 
     if (kv_lo <= kv_hi) {
-        for (int kt = kv_lo & ~(BN - 1); kt <= kv_hi; kt += BN) {
-            __syncthreads();
-            for (int c = tid; c < BN * CPR; c += NTHREADS) {
-                const int r = c / CPR;
-                const int ch = c % CPR;
-                const int key = kt + r;
-                u32x4_t kk = {0u, 0u, 0u, 0u};
-                u32x4_t vv = {0u, 0u, 0u, 0u};
-                if (key < sk) {
-                    const long long g = (long long)(k_start + key) * kv_tok + (long long)kvh * D + ch * 8;
-                    kk = load_u32x4(K + g);
-                    vv = load_u32x4(V + g);
-                }
-                store_u32x4(&sK[r * D + ch * 8], kk);
-                store_u32x4(&sV[r * D + ch * 8], vv);
-            }
-            __syncthreads();
+        const int kt0 = kv_lo & ~(BN - 1);
+        const int ntiles = (kv_hi - kt0) / BN + 1;
+        issue_tile(kt0, 0);
+        wait_vmem();
+        __syncthreads();
+        for (int it = 0; it < ntiles; ++it) {
+            const int kt = kt0 + it * BN;
+            const int buf = it & 1;
+            if (it + 1 < ntiles) issue_tile(kt + BN, buf ^ 1);
 
-            // Wave-uniform: does any row of this wave see a key of this tile?
             const int t_last = kt + BN - 1;
-            if (!wave_has_rows || kt > wlast.hi || t_last < wfirst.lo) continue;
-            // Does every row of this wave see every key of this tile?
-            const bool full = t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
+            if (wave_has_rows && kt <= wlast.hi && t_last >= wfirst.lo) {
+                const bool full = t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
+                const char* sK = smem[buf][0];
+                const char* sV = smem[buf][1];
 
-            f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+                f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, load_u32x4(sK + kb * 32 * ROWB + koff[ks]));
+                        s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
+                    }
+                }
+
+                float mt = -INFINITY;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8_t a = __builtin_bit_cast(
-                        bf16x8_t, load_u32x4(&sK[(kb * 32 + lr) * D + ks * 16 + lh * 8]));
-                    s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
-                }
-            }
-
-            // Logits (log2 units), mask, tile row max.
-            float mt = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float x = score_to_logit<kCap>(s[kb][r], p.x_mul, p.cap_mul, p.cap_out);
-                    if (!full) {
-                        const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                        if (key < mine.lo || key > mine.hi) x = -INFINITY;
-                    }
-                    s[kb][r] = x;
-                    mt = fmaxf(mt, x);
-                }
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt);
-            const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m_run - base);
-            m_run = m_new;
-
-            float psum = 0.0f;
-            uint32_t pk[2][8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const float p0 = fast_exp2(s[kb][r] - base);
-                    const float p1 = fast_exp2(s[kb][r + 1] - base);
-                    psum += p0 + p1;
-                    pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-                }
-            }
-            l_part = l_part * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
-
-            // O^T += V^T P^T. P^T operand (kb, half): registers 8*half..8*half+7 of
-            // S^T block kb, i.e. keys kb*32 + half*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const u32x4_t pv = {pk[kb][half * 4 + 0], pk[kb][half * 4 + 1],
-                                        pk[kb][half * 4 + 2], pk[kb][half * 4 + 3]};
-                    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
-                    const int key0 = kb * 32 + half * 16 + 4 * lh;
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) {
-                        const int col = db * 32 + lr;
-                        uint16_t e[8];
-#pragma unroll
-                        for (int t = 0; t < 4; ++t) {
-                            e[t] = sV[(key0 + t) * D + col];
-                            e[4 + t] = sV[(key0 + 8 + t) * D + col];
+                    for (int r = 0; r < 16; ++r) {
+                        float x = s[kb][r];
+                        if constexpr (kMode == 1) x = x * p.x_mul;
+                        if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
+                        if (!full) {
+                            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                            if (key < mine.lo || key > mine.hi) x = -INFINITY;
                         }
-                        const u32x4_t av = {e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
-                                            e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
-                        acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pb, acc[db]);
+                        s[kb][r] = x;
+                        mt = fmaxf(mt, x);
                     }
                 }
+                mt = fmaxf(mt, __shfl_xor(mt, 32));
+                if constexpr (kMode == 0) mt *= c_exp;  // to log2 units
+                const bool grow = mt > m_run + kLazyRescale;
+                if (wave_any(grow)) {
+                    const float m_new = grow ? mt : m_run;
+                    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+                    m_run = m_new;
+                    l_part *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+                }
+                const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+
+                float psum = 0.0f;
+                uint32_t pk[2][8];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int r = 0; r < 16; r += 2) {
+                        const float p0 = fast_exp2(fmaf(s[kb][r], c_exp, nb));
+                        const float p1 = fast_exp2(fmaf(s[kb][r + 1], c_exp, nb));
+                        psum += p0 + p1;
+                        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+                    }
+                }
+                l_part += psum;
+
+                // O^T += V^T P^T. P^T operand (kb, half): registers 8*half..8*half+7 of
+                // S^T block kb = keys kb*32 + half*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}.
+                uint32_t va[2 * DBLK];
+                const uint32_t vbase = lds_addr(sV);
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db) {
+                    va[2 * db] = vbase + voff[0][db];
+                    va[2 * db + 1] = vbase + voff[1][db];
+                }
+                pv_step<D, 0, 0>(acc, pk, va);
+                pv_step<D, 0, 1>(acc, pk, va);
+                pv_step<D, 1, 0>(acc, pk, va);
+                pv_step<D, 1, 1>(acc, pk, va);
             }
+            wait_vmem();
+            __syncthreads();
         }
     }
 
@@ -228,6 +308,11 @@ __global__ __launch_bounds__(NTHREADS) void fwd_bf16_kernel(const FwdParams p) {
     }
 }
 
+template <int D, int kMode>
+void launch_mode(const FwdParams& p, unsigned grid, hipStream_t stream) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, kMode>), dim3(grid), dim3(NTHREADS), 0, stream, p);
+}
+
 template <int D>
 hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     FwdParams p = args;
@@ -238,9 +323,11 @@ hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+        launch_mode<D, 2>(p, (unsigned)grid, stream);
+    else if (p.scale > 0.0f)
+        launch_mode<D, 0>(p, (unsigned)grid, stream);
     else
-        hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+        launch_mode<D, 1>(p, (unsigned)grid, stream);
     return hipGetLastError();
 }
 

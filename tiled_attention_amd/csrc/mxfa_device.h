@@ -94,6 +94,82 @@ MXFA_DEV u32x4_t load_u32x4(const void* p) { return *reinterpret_cast<const u32x
 MXFA_DEV void store_u32x4(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 MXFA_DEV void store_u32x2(void* p, u32x2_t v) { *reinterpret_cast<u32x2_t*>(p) = v; }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+MXFA_DEV lds_ptr_t to_lds(void* p) { return (lds_ptr_t)p; }
+
+// Buffer resource over [base, base + bytes): loads past the end return zero.
+// Word 3 = 0x00020000: raw (untyped) 32-bit data, the gfx9 setting.
+MXFA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// writes lds_wave_base + 16 * l (the LDS base must be wave uniform).
+MXFA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_wave_base), 16, (int)voffset, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including the
+// LDS-bound buffer loads) have completed.
+MXFA_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane
+// i supplies the address of 4 consecutive 16-bit elements; lane j receives
+// element j % 4 of lanes 4e + j / 4 for e = 0..3. With lane i pointing at row
+// i / 4, columns 4 * (i % 4) .. +3 of a 4 x 16 block, lane j gets column j of
+// rows 0..3.
+MXFA_DEV u32x2_t lds_read_tr16(const void* p) {
+    bf16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Work-group barrier that orders LDS traffic only: this wave's LDS accesses
+// complete, then s_barrier. Unlike __syncthreads() it does not wait for
+// outstanding global loads (e.g. the next tile streaming into LDS).
+MXFA_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+MXFA_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)(p); }
+
+// Batches of transposing LDS reads issued from one asm block that also waits
+// for them (lgkmcnt(0)) before it ends, so no read is in flight when the
+// compiler takes the output registers over. Written in asm because the
+// compiler treats the intrinsic as possibly aliasing in-flight LDS-bound
+// buffer loads and would wait for those first. OFF is a byte offset added to
+// every address (ds immediate offset).
+template <int OFF>
+MXFA_DEV void lds_read_tr16_x4(u32x2_t (&r)[4], const uint32_t (&a)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %1, %5 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %2, %6 offset:%8\n\t"
+        "ds_read_b64_tr_b16 %3, %7 offset:%8\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF)
+        : "memory");
+}
+
+template <int OFF>
+MXFA_DEV void lds_read_tr16_x8(u32x2_t (&r)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
+        : "memory");
+}
+
+MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
 // ---------------------------------------------------------------- work mapping
 
 // Workgroup -> (batch*head unit, q tile), longest work first, XCD aware.
