@@ -20,11 +20,14 @@
 // P^T); the V^T operand comes from LDS through ds_read_b64_tr_b16. O^T keeps
 // one query per lane, so the online-softmax rescale is one multiplier per
 // lane, and it is skipped unless some row's max grew by more than 2^8.
+// Fully visible tiles take a branch without per-element mask tests.
 //
 // K/V tiles are double-buffered in LDS and filled by buffer loads that write
 // LDS directly (out-of-range keys read as zero); the 16-byte chunks of a row
 // are XOR-swizzled so that the K operand reads (16 rows x one chunk) and the
 // transposing V reads (4 rows x 4 chunks per half wave) hit distinct banks.
+#include <type_traits>
+
 #include "mxfa_device.h"
 
 namespace mxfa {
@@ -84,10 +87,10 @@ void fwd_bf16_kernel(const FwdParams p) {
 
     __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];  // [buffer][K, V]
 
-    const WorkItem item = map_workgroup(blockIdx.x, p.units, p.units_per_xcd, p.n_qtiles);
-    if (item.unit < 0) return;
-    const int b = item.unit / p.heads_q;
-    const int h = item.unit % p.heads_q;
+    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
+    if (item.b < 0) return;
+    const int b = item.b;
+    const int h = item.h;
     const int kvh = h / p.group;
     int q_start, sq, k_start, sk;
     if (p.cu_q) {
@@ -196,6 +199,77 @@ void fwd_bf16_kernel(const FwdParams p) {
     float l_part = 0.0f;      // running sum over this lane's keys
     const float c_exp = (kMode == 0) ? p.x_mul : 1.0f;
 
+    // One tile of this wave's 32 rows; kMasked applies the per-element mask.
+    auto tile_body = [&](auto masked_tag, const char* sK, const char* sV, int kt) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, load_u32x4(sK + kb * 32 * ROWB + koff[ks]));
+                s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
+            }
+        }
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = s[kb][r];
+                if constexpr (kMode == 1) x = x * p.x_mul;
+                if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
+                if constexpr (kMasked) {
+                    const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    x = (key >= mine.lo && key <= mine.hi) ? x : -INFINITY;
+                }
+                s[kb][r] = x;
+                mt = fmaxf(mt, x);
+            }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        if constexpr (kMode == 0) mt *= c_exp;  // to log2 units
+        const bool grow = mt > m_run + kLazyRescale;
+        if (wave_any(grow)) {
+            const float m_new = grow ? mt : m_run;
+            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+        }
+        const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+
+        float psum = 0.0f;
+        uint32_t pk[2][8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(fmaf(s[kb][r], c_exp, nb));
+                const float p1 = fast_exp2(fmaf(s[kb][r + 1], c_exp, nb));
+                psum += p0 + p1;
+                pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+            }
+        }
+        l_part += psum;
+
+        // O^T += V^T P^T. P^T operand (kb, half): registers 8*half..8*half+7 of
+        // S^T block kb = keys kb*32 + half*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}.
+        uint32_t va[2 * DBLK];
+        const uint32_t vbase = lds_addr(sV);
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+            va[2 * db] = vbase + voff[0][db];
+            va[2 * db + 1] = vbase + voff[1][db];
+        }
+        pv_step<D, 0, 0>(acc, pk, va);
+        pv_step<D, 0, 1>(acc, pk, va);
+        pv_step<D, 1, 0>(acc, pk, va);
+        pv_step<D, 1, 1>(acc, pk, va);
+    };
+
     if (kv_lo <= kv_hi) {
         const int kt0 = kv_lo & ~(BN - 1);
         const int ntiles = (kv_hi - kt0) / BN + 1;
@@ -210,75 +284,10 @@ void fwd_bf16_kernel(const FwdParams p) {
             const int t_last = kt + BN - 1;
             if (wave_has_rows && kt <= wlast.hi && t_last >= wfirst.lo) {
                 const bool full = t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
-                const char* sK = smem[buf][0];
-                const char* sV = smem[buf][1];
-
-                f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, load_u32x4(sK + kb * 32 * ROWB + koff[ks]));
-                        s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
-                    }
-                }
-
-                float mt = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        float x = s[kb][r];
-                        if constexpr (kMode == 1) x = x * p.x_mul;
-                        if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
-                        if (!full) {
-                            const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                            if (key < mine.lo || key > mine.hi) x = -INFINITY;
-                        }
-                        s[kb][r] = x;
-                        mt = fmaxf(mt, x);
-                    }
-                }
-                mt = fmaxf(mt, __shfl_xor(mt, 32));
-                if constexpr (kMode == 0) mt *= c_exp;  // to log2 units
-                const bool grow = mt > m_run + kLazyRescale;
-                if (wave_any(grow)) {
-                    const float m_new = grow ? mt : m_run;
-                    const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-                    m_run = m_new;
-                    l_part *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
-                }
-                const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
-
-                float psum = 0.0f;
-                uint32_t pk[2][8];
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int r = 0; r < 16; r += 2) {
-                        const float p0 = fast_exp2(fmaf(s[kb][r], c_exp, nb));
-                        const float p1 = fast_exp2(fmaf(s[kb][r + 1], c_exp, nb));
-                        psum += p0 + p1;
-                        pk[kb][r >> 1] = pack_bf16x2(p0, p1);
-                    }
-                }
-                l_part += psum;
-
-                // O^T += V^T P^T. P^T operand (kb, half): registers 8*half..8*half+7 of
-                // S^T block kb = keys kb*32 + half*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}.
-                uint32_t va[2 * DBLK];
-                const uint32_t vbase = lds_addr(sV);
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) {
-                    va[2 * db] = vbase + voff[0][db];
-                    va[2 * db + 1] = vbase + voff[1][db];
-                }
-                pv_step<D, 0, 0>(acc, pk, va);
-                pv_step<D, 0, 1>(acc, pk, va);
-                pv_step<D, 1, 0>(acc, pk, va);
-                pv_step<D, 1, 1>(acc, pk, va);
+                if (full)
+                    tile_body(std::false_type{}, smem[buf][0], smem[buf][1], kt);
+                else
+                    tile_body(std::true_type{}, smem[buf][0], smem[buf][1], kt);
             }
             wait_vmem();
             __syncthreads();
@@ -317,9 +326,7 @@ template <int D>
 hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     FwdParams p = args;
     p.n_qtiles = (p.seqlen_q + BM - 1) / BM;
-    p.units = p.batch * p.heads_q;
-    p.units_per_xcd = (p.units + kXcds - 1) / kXcds;
-    const long long grid = (long long)kXcds * p.n_qtiles * p.units_per_xcd;
+    const long long grid = workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)

@@ -1,27 +1,34 @@
 // fwd_f32.hip -- fp32 attention forward (dense and packed), fp32 throughout.
 //
 // The same tiled online softmax as the bf16 kernel (oxillama-runtime 0.1.0
-// page, src/flash_attention.rs, flash_attention), computed on the vector ALU
-// in fp32 so that fp32 inputs keep fp32 products: one thread per query row,
-// 64 rows per work group (one wave), K/V tiles of 32 keys staged in LDS and
-// read as broadcasts.
+// page, src/flash_attention.rs, flash_attention), on the vector ALU in fp32 so
+// that fp32 inputs keep fp32 products. Work group: 256 threads for 32 query
+// rows; the 8 lanes of a row each take every 8th key of a tile and keep their
+// own running (max, sum, accumulator); the 8 partial states of a row are
+// merged with the max/sum correction at the end (the split combine of the
+// kernelbot amd-mixed-mla submission 588924 page, _reduce_splitk, within a
+// row). K/V tiles are staged in LDS with padded rows, so the 8 different
+// keys a wave reads at once fall on different banks.
 #include "mxfa_device.h"
 
 namespace mxfa {
 namespace {
 
-constexpr int BM = 64;  // query rows per work group (one per lane)
-constexpr int BN = 32;  // keys per tile
+constexpr int NTHREADS = 256;
+constexpr int LPR = 8;                    // lanes per query row
+constexpr int BM = NTHREADS / LPR;        // 32 query rows per work group
+constexpr int BN = 32;                    // keys per tile
 
 template <int D, bool kCap>
-__global__ __launch_bounds__(BM) void fwd_f32_kernel(const FwdParams p) {
-    __shared__ __attribute__((aligned(16))) float sK[BN * D];
-    __shared__ __attribute__((aligned(16))) float sV[BN * D];
+__global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
+    constexpr int RS = D + 4;  // padded LDS row (floats)
+    __shared__ __attribute__((aligned(16))) float sK[BN * RS];
+    __shared__ __attribute__((aligned(16))) float sV[BN * RS];
 
-    const WorkItem item = map_workgroup(blockIdx.x, p.units, p.units_per_xcd, p.n_qtiles);
-    if (item.unit < 0) return;
-    const int b = item.unit / p.heads_q;
-    const int h = item.unit % p.heads_q;
+    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
+    if (item.b < 0) return;
+    const int b = item.b;
+    const int h = item.h;
     const int kvh = h / p.group;
     int q_start, sq, k_start, sk;
     if (p.cu_q) {
@@ -39,6 +46,7 @@ __global__ __launch_bounds__(BM) void fwd_f32_kernel(const FwdParams p) {
     if (tile_row0 >= sq) return;
 
     const int tid = threadIdx.x;
+    const int t = tid % LPR;  // this lane's key phase
     const int off = sk - sq;
     const long long q_tok = (long long)p.heads_q * D;
     const long long kv_tok = (long long)p.heads_kv * D;
@@ -50,14 +58,14 @@ __global__ __launch_bounds__(BM) void fwd_f32_kernel(const FwdParams p) {
     const int kv_lo = visible_range(tile_row0 + off, sk, p.causal, p.window_left, p.window_right).lo;
     const int kv_hi = visible_range(row_last + off, sk, p.causal, p.window_left, p.window_right).hi;
 
-    const int qi = tile_row0 + tid;
+    const int qi = tile_row0 + tid / LPR;
     const bool q_valid = qi < sq;
     const KeyRange mine = visible_range(qi + off, sk, p.causal, p.window_left, p.window_right);
 
     float q[D];
     float acc[D];
     {
-        const float* qp = Q + (long long)(q_start + qi) * q_tok + (long long)h * D;
+        const float* qp = Q + (long long)(q_start + (q_valid ? qi : 0)) * q_tok + (long long)h * D;
 #pragma unroll
         for (int c = 0; c < D; c += 4) {
             f32x4_t v = {0.f, 0.f, 0.f, 0.f};
@@ -70,13 +78,13 @@ __global__ __launch_bounds__(BM) void fwd_f32_kernel(const FwdParams p) {
     }
 #pragma unroll
     for (int c = 0; c < D; ++c) acc[c] = 0.0f;
-    float m_run = -INFINITY;
+    float m_run = -INFINITY;  // log2 units
     float l_run = 0.0f;
 
     if (kv_lo <= kv_hi) {
         for (int kt = kv_lo & ~(BN - 1); kt <= kv_hi; kt += BN) {
             __syncthreads();
-            for (int c = tid; c < BN * D / 4; c += BM) {
+            for (int c = tid; c < BN * D / 4; c += NTHREADS) {
                 const int r = c / (D / 4);
                 const int ch = c % (D / 4);
                 const int key = kt + r;
@@ -87,52 +95,85 @@ __global__ __launch_bounds__(BM) void fwd_f32_kernel(const FwdParams p) {
                     kk = *reinterpret_cast<const f32x4_t*>(K + g);
                     vv = *reinterpret_cast<const f32x4_t*>(V + g);
                 }
-                *reinterpret_cast<f32x4_t*>(&sK[r * D + ch * 4]) = kk;
-                *reinterpret_cast<f32x4_t*>(&sV[r * D + ch * 4]) = vv;
+                *reinterpret_cast<f32x4_t*>(&sK[r * RS + ch * 4]) = kk;
+                *reinterpret_cast<f32x4_t*>(&sV[r * RS + ch * 4]) = vv;
             }
             __syncthreads();
-            if (!q_valid) continue;
 
-            float x[BN];
+            float x[BN / LPR];
             float mt = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < BN; ++j) {
+            for (int jj = 0; jj < BN / LPR; ++jj) {
+                const int j = jj * LPR + t;
                 float s = 0.0f;
 #pragma unroll
-                for (int c = 0; c < D; ++c) s = fmaf(q[c], sK[j * D + c], s);
-                float t = score_to_logit<kCap>(s, p.x_mul, p.cap_mul, p.cap_out);
+                for (int c = 0; c < D; c += 4) {
+                    const f32x4_t kv4 = *reinterpret_cast<const f32x4_t*>(&sK[j * RS + c]);
+                    s = fmaf(q[c], kv4[0], s);
+                    s = fmaf(q[c + 1], kv4[1], s);
+                    s = fmaf(q[c + 2], kv4[2], s);
+                    s = fmaf(q[c + 3], kv4[3], s);
+                }
+                float lg = score_to_logit<kCap>(s, p.x_mul, p.cap_mul, p.cap_out);
                 const int key = kt + j;
-                if (key < mine.lo || key > mine.hi) t = -INFINITY;
-                x[j] = t;
-                mt = fmaxf(mt, t);
+                if (key < mine.lo || key > mine.hi) lg = -INFINITY;
+                x[jj] = lg;
+                mt = fmaxf(mt, lg);
             }
-            const float m_new = fmaxf(m_run, mt);
-            const float base = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = fast_exp2(m_run - base);
-            m_run = m_new;
-            l_run *= alpha;
+            if (mt > m_run) {
+                const float alpha = fast_exp2(m_run - mt);  // m_run = -inf -> 0
+                m_run = mt;
+                l_run *= alpha;
 #pragma unroll
-            for (int c = 0; c < D; ++c) acc[c] *= alpha;
+                for (int c = 0; c < D; ++c) acc[c] *= alpha;
+            }
+            const float base = (m_run == -INFINITY) ? 0.0f : m_run;
 #pragma unroll
-            for (int j = 0; j < BN; ++j) {
-                const float pj = fast_exp2(x[j] - base);
+            for (int jj = 0; jj < BN / LPR; ++jj) {
+                const int j = jj * LPR + t;
+                const float pj = fast_exp2(x[jj] - base);
                 l_run += pj;
 #pragma unroll
-                for (int c = 0; c < D; ++c) acc[c] = fmaf(pj, sV[j * D + c], acc[c]);
+                for (int c = 0; c < D; c += 4) {
+                    const f32x4_t v4 = *reinterpret_cast<const f32x4_t*>(&sV[j * RS + c]);
+                    acc[c] = fmaf(pj, v4[0], acc[c]);
+                    acc[c + 1] = fmaf(pj, v4[1], acc[c + 1]);
+                    acc[c + 2] = fmaf(pj, v4[2], acc[c + 2]);
+                    acc[c + 3] = fmaf(pj, v4[3], acc[c + 3]);
+                }
             }
         }
     }
 
+    // Merge the 8 lanes of the row: M = max m_t, w_t = exp2(m_t - M),
+    // l = sum w_t l_t, acc = sum w_t acc_t.
+    float M = m_run;
+#pragma unroll
+    for (int s = 1; s < LPR; s <<= 1) M = fmaxf(M, __shfl_xor(M, s));
+    const float w = (M == -INFINITY) ? 0.0f : fast_exp2(m_run - M);
+    float l = l_run * w;
+#pragma unroll
+    for (int s = 1; s < LPR; s <<= 1) l += __shfl_xor(l, s);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        float a = acc[c] * w;
+#pragma unroll
+        for (int s = 1; s < LPR; s <<= 1) a += __shfl_xor(a, s);
+        acc[c] = a;
+    }
     if (!q_valid) return;
-    const float inv = (l_run > 0.0f) ? 1.0f / l_run : 0.0f;
+    const float inv = (l > 0.0f) ? 1.0f / l : 0.0f;
     float* O = static_cast<float*>(p.o) + (long long)(q_start + qi) * q_tok + (long long)h * D;
+    // Lane t of the row writes channels [t*D/8, (t+1)*D/8).
 #pragma unroll
     for (int c = 0; c < D; c += 4) {
-        const f32x4_t v = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
-        *reinterpret_cast<f32x4_t*>(O + c) = v;
+        if (c / (D / LPR) == t) {
+            const f32x4_t v = {acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv};
+            *reinterpret_cast<f32x4_t*>(O + c) = v;
+        }
     }
-    if (p.lse) {
-        const float lse = (l_run > 0.0f) ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
+    if (p.lse && t == 0) {
+        const float lse = (l > 0.0f) ? (M + fast_log2(l)) * kLn2 : -INFINITY;
         const long long idx = p.cu_q ? (long long)h * p.total_q + q_start + qi
                                      : ((long long)b * p.heads_q + h) * sq + qi;
         p.lse[idx] = lse;
@@ -143,15 +184,13 @@ template <int D>
 hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     FwdParams p = args;
     p.n_qtiles = (p.seqlen_q + BM - 1) / BM;
-    p.units = p.batch * p.heads_q;
-    p.units_per_xcd = (p.units + kXcds - 1) / kXcds;
-    const long long grid = (long long)kXcds * p.n_qtiles * p.units_per_xcd;
+    const long long grid = workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(BM), 0, stream, p);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(BM), 0, stream, p);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -172,28 +172,44 @@ MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 
 // ---------------------------------------------------------------- work mapping
 
-// Workgroup -> (batch*head unit, q tile), longest work first, XCD aware.
+// Workgroup -> (batch, query head, q tile), longest work first, XCD aware.
 // Workgroups are handed to the 8 XCDs round-robin by linear id, so id i runs
-// on XCD i % 8. Each XCD owns a contiguous range of (batch, head) units -- the
-// query heads of one kv head are adjacent, so they share K/V in that XCD's
-// L2 -- and walks its units' q tiles from the last (most keys under a causal
-// mask) to the first.
+// on XCD i % 8. KV groups (batch, kv head) are dealt to the XCDs round-robin
+// (group g -> XCD g % 8), so every XCD gets a share of every sequence, and the
+// query heads of one kv group stay on one XCD, where they share K/V in its
+// L2. Each XCD walks its items by q tile from the last (most keys under a
+// causal mask) to the first.
 struct WorkItem {
-    int unit;   // b * heads_q + h, or -1 for a padding workgroup
+    int b;      // batch / segment, or -1 for a padding workgroup
+    int h;      // query head
     int qtile;
 };
 
-MXFA_DEV WorkItem map_workgroup(int id, int units, int units_per_xcd, int n_qtiles) {
+MXFA_DEV WorkItem map_workgroup(int id, int batch, int heads_kv, int group, int n_qtiles) {
     const int x = id % kXcds;
     const int n = id / kXcds;
-    const int u0 = (int)(((long long)x * units) / kXcds);
-    const int u1 = (int)(((long long)(x + 1) * units) / kXcds);
-    const int rank = n / units_per_xcd;
-    const int j = n % units_per_xcd;
+    const int groups = batch * heads_kv;
+    const int groups_per_xcd = (groups + kXcds - 1) / kXcds;
+    const int per_rank = groups_per_xcd * group;
+    const int rank = n / per_rank;
+    const int rem = n % per_rank;
+    const int g = (rem / group) * kXcds + x;
     WorkItem w;
-    w.unit = (u0 + j < u1 && rank < n_qtiles) ? u0 + j : -1;
     w.qtile = n_qtiles - 1 - rank;
+    if (g >= groups || rank >= n_qtiles) {
+        w.b = -1;
+        w.h = 0;
+        return w;
+    }
+    w.b = g / heads_kv;
+    w.h = (g % heads_kv) * group + rem % group;
     return w;
+}
+
+// Grid size for map_workgroup.
+inline long long workgroup_count(int batch, int heads_kv, int group, int n_qtiles) {
+    const long long groups = (long long)batch * heads_kv;
+    return (long long)kXcds * ((groups + kXcds - 1) / kXcds) * group * n_qtiles;
 }
 
 }  // namespace mxfa

@@ -33,9 +33,7 @@ struct FwdParams {
     float x_mul;             // score -> log2-domain logit multiplier (no cap: scale*log2e)
     float cap_mul;           // cap: 2*log2e*scale/cap
     float cap_out;           // cap: cap*log2e
-    int n_qtiles;            // ceil(seqlen_q / BM)
-    int units;               // batch * heads_q
-    int units_per_xcd;       // ceil(units / 8)
+    int n_qtiles;            // ceil(seqlen_q / BM), set by the launcher
 };
 
 // One latent-KV split decode.
