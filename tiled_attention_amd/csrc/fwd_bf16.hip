@@ -20,12 +20,17 @@
 // P^T); the V^T operand comes from LDS through ds_read_b64_tr_b16. O^T keeps
 // one query per lane, so the online-softmax rescale is one multiplier per
 // lane, and it is skipped unless some row's max grew by more than 2^8.
-// Fully visible tiles take a branch without per-element mask tests.
 //
-// K/V tiles are double-buffered in LDS and filled by buffer loads that write
-// LDS directly (out-of-range keys read as zero); the 16-byte chunks of a row
-// are XOR-swizzled so that the K operand reads (16 rows x one chunk) and the
-// transposing V reads (4 rows x 4 chunks per half wave) hit distinct banks.
+// Software pipeline inside each wave (two S register sets): while the MFMAs
+// compute S for tile j+1, the vector ALU turns S of tile j into P; while the
+// MFMAs accumulate P V for tile j, the vector ALU masks tile j+1 and takes
+// its row max. K therefore runs one tile ahead of V: K tiles j+1 (in use) and
+// j+2 (arriving), V tiles j (in use) and j+1 (arriving) share two buffers
+// each, filled by buffer loads that write LDS directly (out-of-range keys
+// read as zero). The 16-byte chunks of a row are XOR-swizzled so that the K
+// operand reads (16 rows x one chunk) and the transposing V reads (4 rows x 4
+// chunks per half wave) hit distinct banks. Fully visible tiles take a branch
+// without per-element mask tests.
 #include <type_traits>
 
 #include "mxfa_device.h"
@@ -85,7 +90,8 @@ void fwd_bf16_kernel(const FwdParams p) {
     constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
     constexpr int LOADS = TILEB / (16 * NTHREADS);  // 16-byte loads per thread per tile
 
-    __shared__ __attribute__((aligned(1024))) char smem[2][2][TILEB];  // [buffer][K, V]
+    __shared__ __attribute__((aligned(TILEB))) char sK[2][TILEB];
+    __shared__ __attribute__((aligned(TILEB))) char sV[2][TILEB];
 
     const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (item.b < 0) return;
@@ -121,12 +127,12 @@ void fwd_bf16_kernel(const FwdParams p) {
     const int kv_lo = visible_range(tile_row0 + off, sk, p.causal, p.window_left, p.window_right).lo;
     const int kv_hi = visible_range(row_last + off, sk, p.causal, p.window_left, p.window_right).hi;
 
-    // This wave's rows and their key range.
+    // This wave's rows and their key range (decides fully visible tiles).
     const int wrow0 = tile_row0 + wave * 32;
-    const int wrow_last = min(wrow0 + 31, sq - 1);
-    const bool wave_has_rows = wrow0 < sq;
+    const int wrow_last = max(min(wrow0 + 31, sq - 1), wrow0);
     const KeyRange wfirst = visible_range(wrow0 + off, sk, p.causal, p.window_left, p.window_right);
     const KeyRange wlast = visible_range(wrow_last + off, sk, p.causal, p.window_left, p.window_right);
+    const bool wave_rows_valid = wrow0 < sq;
 
     // This lane's query row and its visible keys.
     const int qi = wrow0 + lr;
@@ -146,14 +152,16 @@ void fwd_bf16_kernel(const FwdParams p) {
         }
     }
 
-    // LDS read offsets (bytes within a tile). K operand: row kb*32 + lr, chunk ks*2 + lh.
-    const int f_lr = swz<D>(lr & 15);
-    int koff[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = lr * ROWB + (((ks * 2 + lh) ^ f_lr) << 4);
+    // LDS read offsets. Tiles are 16 KB aligned (D = 128; 8 KB for D = 64) and
+    // the swizzle only moves bits inside a row, so a read address is
+    // tile_base + (lane constant XOR step constant).
+    // K operand: row kb*32 + lr, chunk (ks*2 + lh) ^ swz(lr) ->
+    //   (kx ^ (ks << 5)) + kb*32*ROWB with kx = lr*ROWB | ((lh ^ swz(lr)) << 4).
+    const uint32_t kx = (uint32_t)(lr * ROWB) | (uint32_t)((lh ^ swz<D>(lr & 15)) << 4);
     // V^T operand via transposing reads: 16-lane group g, lane i reads row
-    // (which*8 + 4*(g/2) + i/4) of a 16-key step, columns db*32 + (g%2)*16 + 4*(i%4).
-    int voff[2][DBLK];
+    // (which*8 + 4*(g/2) + i/4) of a 16-key step, columns db*32 + (g%2)*16 + 4*(i%4):
+    //   chunk (db*4 + cl) ^ swz(row) -> vx[which] ^ (db << 6).
+    uint32_t vx[2];
     {
         const int g = lane >> 4;
         const int i = lane & 15;
@@ -161,35 +169,26 @@ void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             const int rowl = which * 8 + 4 * (g >> 1) + (i >> 2);
-            const int fw = swz<D>(rowl);
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-                voff[which][db] = rowl * ROWB + (((db * 4 + cl) ^ fw) << 4) + (i & 1) * 8;
+            vx[which] = (uint32_t)(rowl * ROWB) | (uint32_t)((cl ^ swz<D>(rowl)) << 4) | (uint32_t)((i & 1) * 8);
         }
     }
-    // Global -> LDS loads: 16-byte chunk position P = n*256 + tid of a tile.
-    uint32_t goff[LOADS];
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-        const int P = n * NTHREADS + tid;
-        const int row = P / CPR;
-        const int c = (P % CPR) ^ swz<D>(row & 15);
-        goff[n] = (uint32_t)(((long long)row * kv_tok + c * 8) * 2);
-    }
+    // Global -> LDS loads: 16-byte chunk position P = n*256 + tid of a tile, i.e.
+    // row n*(256/CPR) + tid/CPR, chunk tid%CPR; the swizzle depends on the row
+    // only through row % 16, which is the same for every n.
+    const int lrow = tid / CPR;
+    const uint32_t goff = (uint32_t)(((long long)lrow * kv_tok + (((tid % CPR) ^ swz<D>(lrow & 15)) * 8)) * 2);
+    const uint32_t gstep = (uint32_t)((NTHREADS / CPR) * kv_tok * 2);
     const uint16_t* Kseg = static_cast<const uint16_t*>(p.k) + (long long)k_start * kv_tok + (long long)kvh * D;
     const uint16_t* Vseg = static_cast<const uint16_t*>(p.v) + (long long)k_start * kv_tok + (long long)kvh * D;
-
-    auto issue_tile = [&](int kt, int buf) {
-        // Bytes of the tile that hold keys < sk (keys past the end read as zero).
+    // Bytes from key kt on that hold keys < sk (keys past the end read as zero).
+    auto tile_bytes = [&](int kt) -> uint32_t {
         long long bytes = (long long)(sk - kt - 1) * kv_tok * 2 + D * 2;
-        if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-        const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kseg + (long long)kt * kv_tok, (uint32_t)bytes);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vseg + (long long)kt * kv_tok, (uint32_t)bytes);
+        return (uint32_t)(bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+    };
+    auto issue = [&](const uint16_t* seg, int kt, char* tile) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(seg + (long long)kt * kv_tok, tile_bytes(kt));
 #pragma unroll
-        for (int n = 0; n < LOADS; ++n) {
-            buffer_load_lds16(rk, &smem[buf][0][(n * NTHREADS + wave * 64) * 16], goff[n]);
-            buffer_load_lds16(rv, &smem[buf][1][(n * NTHREADS + wave * 64) * 16], goff[n]);
-        }
+        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, tile + (n * NTHREADS + wave * 64) * 16, goff, n * gstep);
     };
 
     f32x16_t acc[DBLK];
@@ -199,20 +198,26 @@ void fwd_bf16_kernel(const FwdParams p) {
     float l_part = 0.0f;      // running sum over this lane's keys
     const float c_exp = (kMode == 0) ? p.x_mul : 1.0f;
 
-    // One tile of this wave's 32 rows; kMasked applies the per-element mask.
-    auto tile_body = [&](auto masked_tag, const char* sK, const char* sV, int kt) {
-        constexpr bool kMasked = decltype(masked_tag)::value;
-        f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    // ---- pipeline pieces
+    // S^T = K Q^T for one tile.
+    auto qk = [&](f32x16_t (&s)[2], const char* kt_lds) {
+        s[0] = f32x16_t{};
+        s[1] = f32x16_t{};
+        const uint32_t kb0 = lds_addr(kt_lds) + kx;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
+            const uint32_t a0 = kb0 ^ (uint32_t)(ks << 5);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, load_u32x4(sK + kb * 32 * ROWB + koff[ks]));
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_load16(a0 + kb * 32 * ROWB));
                 s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
             }
         }
-
-        float mt = -INFINITY;
+    };
+    // Logits (raw scores in mode 0), mask, and the tile's row max in log2 units.
+    auto logits_max = [&](auto masked_tag, f32x16_t (&s)[2], int kt) -> float {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        float m = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -225,11 +230,19 @@ void fwd_bf16_kernel(const FwdParams p) {
                     x = (key >= mine.lo && key <= mine.hi) ? x : -INFINITY;
                 }
                 s[kb][r] = x;
-                mt = fmaxf(mt, x);
+                m = fmaxf(m, x);
             }
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        if constexpr (kMode == 0) mt *= c_exp;  // to log2 units
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if constexpr (kMode == 0) m *= c_exp;
+        return m;
+    };
+    auto tile_full = [&](int kt) {
+        const int t_last = kt + BN - 1;
+        return wave_rows_valid && t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
+    };
+    // Lazy max update: rescale only when some row's max grew by more than 2^8.
+    auto update_max = [&](float mt) {
         const bool grow = mt > m_run + kLazyRescale;
         if (wave_any(grow)) {
             const float m_new = grow ? mt : m_run;
@@ -239,10 +252,12 @@ void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
         }
+    };
+    // P = exp2(logit - max) as bf16 pairs; P^T operand (kb, half) = registers
+    // 8*half..8*half+7 of S^T block kb.
+    auto exp_tile = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8]) {
         const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
-
         float psum = 0.0f;
-        uint32_t pk[2][8];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -254,15 +269,16 @@ void fwd_bf16_kernel(const FwdParams p) {
             }
         }
         l_part += psum;
-
-        // O^T += V^T P^T. P^T operand (kb, half): registers 8*half..8*half+7 of
-        // S^T block kb = keys kb*32 + half*16 + {4*lh + 0..3, 8 + 4*lh + 0..3}.
+    };
+    // O^T += V^T P^T for one tile.
+    auto pv = [&](const uint32_t (&pk)[2][8], const char* vt_lds) {
         uint32_t va[2 * DBLK];
-        const uint32_t vbase = lds_addr(sV);
+        const uint32_t v0 = lds_addr(vt_lds) + vx[0];
+        const uint32_t v1 = lds_addr(vt_lds) + vx[1];
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-            va[2 * db] = vbase + voff[0][db];
-            va[2 * db + 1] = vbase + voff[1][db];
+            va[2 * db] = v0 ^ (uint32_t)(db << 6);
+            va[2 * db + 1] = v1 ^ (uint32_t)(db << 6);
         }
         pv_step<D, 0, 0>(acc, pk, va);
         pv_step<D, 0, 1>(acc, pk, va);
@@ -273,24 +289,57 @@ void fwd_bf16_kernel(const FwdParams p) {
     if (kv_lo <= kv_hi) {
         const int kt0 = kv_lo & ~(BN - 1);
         const int ntiles = (kv_hi - kt0) / BN + 1;
-        issue_tile(kt0, 0);
+        // Prologue: K0, V0, K1 in flight; S and row max of tile 0.
+        issue(Kseg, kt0, sK[0]);
+        issue(Vseg, kt0, sV[0]);
+        if (ntiles > 1) issue(Kseg, kt0 + BN, sK[1]);
         wait_vmem();
         __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-            const int kt = kt0 + it * BN;
-            const int buf = it & 1;
-            if (it + 1 < ntiles) issue_tile(kt + BN, buf ^ 1);
+        f32x16_t sa[2], sb[2];
+        float mt_a = -INFINITY, mt_b = -INFINITY;
+        qk(sa, sK[0]);
+        mt_a = tile_full(kt0) ? logits_max(std::false_type{}, sa, kt0) : logits_max(std::true_type{}, sa, kt0);
+        lds_barrier();  // every wave is done with K0 before K2 overwrites it
 
-            const int t_last = kt + BN - 1;
-            if (wave_has_rows && kt <= wlast.hi && t_last >= wfirst.lo) {
-                const bool full = t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
-                if (full)
-                    tile_body(std::false_type{}, smem[buf][0], smem[buf][1], kt);
-                else
-                    tile_body(std::true_type{}, smem[buf][0], smem[buf][1], kt);
+        // Tile j: S_j in s_cur (masked, max mt_cur); K(j+1) and V(j) resident.
+        auto step = [&](auto has_next_tag, int j, f32x16_t (&s_cur)[2], float mt_cur, f32x16_t (&s_next)[2],
+                        float& mt_next) {
+            constexpr bool kNext = decltype(has_next_tag)::value;
+            const int kt = kt0 + j * BN;
+            if (j + 2 < ntiles) issue(Kseg, kt + 2 * BN, sK[j & 1]);
+            if (j + 1 < ntiles) issue(Vseg, kt + BN, sV[(j + 1) & 1]);
+            update_max(mt_cur);
+            uint32_t pk[2][8];
+            if constexpr (kNext) {
+                // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
+                qk(s_next, sK[(j + 1) & 1]);
+                exp_tile(s_cur, pk);
+                // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
+                if (tile_full(kt + BN)) {
+                    pv(pk, sV[j & 1]);
+                    mt_next = logits_max(std::false_type{}, s_next, kt + BN);
+                } else {
+                    pv(pk, sV[j & 1]);
+                    mt_next = logits_max(std::true_type{}, s_next, kt + BN);
+                }
+            } else {
+                exp_tile(s_cur, pk);
+                pv(pk, sV[j & 1]);
             }
             wait_vmem();
             __syncthreads();
+        };
+
+        int j = 0;
+        for (; j + 2 < ntiles; j += 2) {
+            step(std::true_type{}, j, sa, mt_a, sb, mt_b);
+            step(std::true_type{}, j + 1, sb, mt_b, sa, mt_a);
+        }
+        if (j + 1 < ntiles) {
+            step(std::true_type{}, j, sa, mt_a, sb, mt_b);
+            step(std::false_type{}, j + 1, sb, mt_b, sa, mt_a);
+        } else {
+            step(std::false_type{}, j, sa, mt_a, sb, mt_b);
         }
     }
 

@@ -106,8 +106,15 @@ MXFA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
 // writes lds_wave_base + 16 * l (the LDS base must be wave uniform).
-MXFA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voffset) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_wave_base), 16, (int)voffset, 0, 0, 0);
+MXFA_DEV void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_wave_base, uint32_t voffset,
+                                uint32_t soffset = 0) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, to_lds(lds_wave_base), 16, (int)voffset, (int)soffset, 0, 0);
+}
+
+// 16 bytes per lane from global memory into registers through a buffer
+// resource (reads past the resource's end return zero).
+MXFA_DEV u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voffset, uint32_t soffset) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voffset, (int)soffset, 0));
 }
 
 // Wait until this wave's outstanding vector-memory operations (including the
@@ -166,6 +173,11 @@ MXFA_DEV void lds_read_tr16_x8(u32x2_t (&r)[8], const uint32_t (&a)[8]) {
           "=&v"(r[7])
         : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF)
         : "memory");
+}
+
+// 16-byte LDS read at a byte address (ds_read_b128).
+MXFA_DEV u32x4_t lds_load16(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((size_t)addr);
 }
 
 MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
