@@ -213,6 +213,24 @@ def test_decode_matches_oracle(case):
             str(case))
 
 
+@pytest.mark.parametrize("scale", [-1.0 / math.sqrt(576), 0.0])
+def test_decode_nonpositive_scale(scale):
+    # A negative scale turns the largest score into the smallest logit; zero
+    # gives uniform weights. Both must follow the oracle like any other scale.
+    p = workloads.make_problem(3200, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=[4, 2],
+                               lens_k=[300, 97], shared_kv=True)
+    print(f"[decode] scale={scale}", flush=True)
+    o_g, lse_g = _run_decode(p, 16, False, (-1, -1), 0.0, 2, scale)
+    kv = to_np(p["kv"])
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kv, kv[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), causal=False, window=(-1, -1),
+                                              softcap=0.0, scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            f"scale={scale}")
+
+
 def test_decode_independent_of_split_count():
     p = workloads.make_problem(3100, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=[4, 4, 1],
                                lens_k=[2000, 333, 64], shared_kv=True)

@@ -36,6 +36,15 @@ def compile_flags() -> list:
             "-I", INCLUDE, "-I", CSRC]
 
 
+# Extra flags per source. The decode kernel keeps 128 fp32 accumulators per
+# lane live next to its Q^T operand; left to its heuristics the compiler
+# moves them between VGPRs and AGPRs around every tile, so its MFMAs are
+# pinned to the VGPR form.
+FILE_FLAGS = {
+    "decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
     """Compile every HIP source and link libmxfa.so; returns the library path."""
     hipcc = _hipcc()
@@ -47,7 +56,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
 
     def compile_one(src_obj):
         src, obj = src_obj
-        cmd = [hipcc, *compile_flags(), "-c", src, "-o", obj]
+        cmd = [hipcc, *compile_flags(), *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = r.stdout + r.stderr
         # the host pass does not know the device-only feature flag

@@ -10,17 +10,26 @@
 //
 // Split kernel: one work group (4 waves, one per SIMD, one group per CU)
 // owns 64 rows = (query token, head of the kv group) pairs of one sequence
-// and one key split. Latent tiles of 64 keys x 576 channels (72 KB) are
-// double-buffered in LDS and filled by buffer loads that write LDS directly,
-// so the next tile streams in while the current one is computed. Per tile:
-//   QK: wave w computes the S^T block (keys 32*(w/2).., rows 32*(w%2)..) with
-//       36 steps of v_mfma_f32_32x32x16_bf16 (Q^T lives in registers);
-//   softmax: the two waves of a row block exchange their row maxima in LDS
-//       and write P (bf16) and each row's rescale factor to LDS;
-//   PV: wave w owns 128 of the 512 output channels for all 64 rows and
-//       accumulates O^T = V^T P^T with the V^T operand read by
-//       ds_read_b64_tr_b16; the rescale is skipped when no row max grew.
+// and one key split. The latent rows stream from HBM through four 36 KB LDS
+// stages (32-key tiles) filled by buffer loads that write LDS directly; each
+// wave waits only for the tile it needs (vmcnt with the count of later
+// loads). The steps are software pipelined: while tile j's P V runs, tile
+// j+1 is read for its scores and tiles j+2 and j+3 stream in.
+// Wave w = (rb, ch) with rb = w % 2 (rows 32*rb..+31) and ch = w / 2:
+//   QK: the partial S^T (32 keys x 32 rows) over channels 288*ch..+287 with
+//       18 v_mfma_f32_32x32x16_bf16 (its Q^T slice lives in accumulation
+//       registers); the two waves of a row block swap partials through LDS
+//       and both add them (same operands, same order: the same S^T);
+//   softmax: mask, row max (one lane exchange), lazy rescale, exp2, done
+//       identically by both waves of the row block;
+//   PV: O^T (channels 256*ch..+255 x 32 rows) += V^T P^T with 16 MFMAs;
+//       P^T is the S^T accumulator re-packed to bf16 in place and the V^T
+//       operand comes from ds_read_b64_tr_b16 in the matching key order.
+// Splitting the contraction keeps the 32x32x16 MFMA shape (twice the rate of
+// 16x16x32 on this chip) and halves the LDS bytes each wave reads per tile.
 // Combine kernel: one thread per (row, 16 channels) merges the splits.
+#include <type_traits>
+
 #include "mxfa_device.h"
 
 namespace mxfa {
@@ -28,49 +37,37 @@ namespace {
 
 constexpr int DQK = 576;
 constexpr int DV = 512;
-constexpr int BN = 64;                   // keys per tile
-constexpr int ROWS = kDecodeRows;        // 64
+constexpr int BN = kDecodeTile;          // 32 keys per tile
+constexpr int ROWS = kDecodeRows;        // 64 rows per work group
 constexpr int NTHREADS = 256;
-constexpr int KSTEPS = DQK / 16;         // 36
+constexpr int STAGES = 4;                // LDS tiles; STAGES - 1 in flight
+constexpr int KSTEPS = DQK / 16 / 2;     // 18 contraction steps of 16 channels per wave
+constexpr int CBLK = DV / 32 / 2;        // 8 blocks of 32 output channels per wave
 constexpr int ROWB = DQK * 2;            // 1152 bytes per latent row
 constexpr int CPR = DQK / 8;             // 72 chunks of 16 bytes per row
-constexpr int TILEB = BN * ROWB;         // 73728 bytes per tile
-constexpr int LOADS = BN * CPR / NTHREADS;  // 18 chunks per thread per tile
-constexpr int PSTR = BN + 8;             // padded P row (elements): 144 bytes, conflict-free 16-byte reads
+constexpr int TILEB = BN * ROWB;         // 36864 bytes per tile
+constexpr int LOADS = TILEB / (16 * NTHREADS);  // 9 loads per thread per tile
 constexpr float kLazyRescale = 8.0f;
+static_assert(LOADS * 16 * NTHREADS == TILEB, "tile must split into whole loads");
 
-// 1152-byte rows put consecutive rows 8 chunks apart in the 16-chunk bank
-// line; this XOR (< 8, so it stays inside a row's aligned 8-chunk groups)
-// makes 16 consecutive rows x one chunk, and 4 consecutive rows x an aligned
-// group of 4 chunks, fall on distinct banks.
+// Chunk swizzle of a 1152-byte row (physical chunk = logical ^ swz(row)).
+// Rows alternate between the two halves of the 16-chunk bank line; the XOR
+// (< 8, so a chunk stays in its aligned group of 8 and inside the row)
+// spreads 16 consecutive rows x one chunk over all 16 bank slots (K operand
+// reads) and 4 consecutive rows x an aligned group of 4 chunks likewise
+// (transposing V reads).
 MXFA_DEV int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
-
-// One 16-key step (keys K4*16 + 8*lh + 0..7 of the tile) of O^T += V^T P^T for
-// this wave's 128 channels and both 32-row blocks.
-template <int K4>
-MXFA_DEV void pv_k4(f32x16_t (&acc)[4][2], const uint32_t (&va)[8], const uint16_t* sP, int lr, int lh) {
-    const bf16x8_t p0 = __builtin_bit_cast(bf16x8_t, load_u32x4(sP + lr * PSTR + K4 * 16 + lh * 8));
-    const bf16x8_t p1 = __builtin_bit_cast(bf16x8_t, load_u32x4(sP + (32 + lr) * PSTR + K4 * 16 + lh * 8));
-    u32x2_t r[8];
-    lds_read_tr16_x8<K4 * 16 * ROWB>(r, va);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        const u32x4_t av = {r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-        acc[db][0] = mfma32x32x16(a, p0, acc[db][0]);
-        acc[db][1] = mfma32x32x16(a, p1, acc[db][1]);
-    }
-}
 
 template <bool kCap>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_kernel(const DecodeParams p) {
-    extern __shared__ __attribute__((aligned(1024))) char dsmem[];
-    char* sKV = dsmem;                                        // [2][TILEB]
-    uint16_t* sP = reinterpret_cast<uint16_t*>(dsmem + 2 * TILEB);  // [ROWS][PSTR]
-    float* sMax = reinterpret_cast<float*>(dsmem + 2 * TILEB + ROWS * PSTR * 2);  // [2][ROWS]
-    float* sAlpha = sMax + 2 * ROWS;                          // [ROWS]
-    float* sSum = sAlpha + ROWS;                              // [2][ROWS]
+    // Five LDS objects: a reader of one stage then never waits for the loads
+    // streaming into the others.
+    __shared__ __attribute__((aligned(1024))) char sT0[TILEB];
+    __shared__ __attribute__((aligned(1024))) char sT1[TILEB];
+    __shared__ __attribute__((aligned(1024))) char sT2[TILEB];
+    __shared__ __attribute__((aligned(1024))) char sT3[TILEB];
+    __shared__ __attribute__((aligned(1024))) f32x4_t sS[4][4][64];  // partial S^T per wave: [wave][r/4][lane]
 
     int id = blockIdx.x;
     const int sp = id % p.splits;
@@ -91,18 +88,17 @@ void decode_split_kernel(const DecodeParams p) {
     const int off = sk - sq;
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    const int rb = w & 1;
+    const int ch = w >> 1;
     const int lane = tid & 63;
-    const int lr = lane & 31;
+    const int lr = lane & 31;  // S^T / O^T column: row 32*rb + lr of the group
     const int lh = lane >> 5;
-    const int kb = w >> 1;  // key block of this wave's S^T block
-    const int rb = w & 1;   // row block of this wave's S^T block
 
     // Keys any row of the group can see, cut to this split (splits are tile aligned).
-    const int tok_first = row0 / G;
-    const int tok_last = min(row0 + ROWS - 1, nrows - 1) / G;
-    const KeyRange first = visible_range(tok_first + off, sk, p.causal, p.window_left, p.window_right);
-    const KeyRange last = visible_range(tok_last + off, sk, p.causal, p.window_left, p.window_right);
+    const int last_row = min(row0 + ROWS, nrows) - 1;
+    const KeyRange first = visible_range(row0 / G + off, sk, p.causal, p.window_left, p.window_right);
+    const KeyRange last = visible_range(last_row / G + off, sk, p.causal, p.window_left, p.window_right);
     const int ntiles_all = (sk + BN - 1) / BN;
     const int tiles_per_split = (ntiles_all + p.splits - 1) / p.splits;
     const int s_lo = sp * tiles_per_split * BN;
@@ -110,192 +106,316 @@ void decode_split_kernel(const DecodeParams p) {
     const int lo = max(first.lo, s_lo);
     const int hi = min(last.hi, s_hi);
 
-    // This lane's S^T column: row rb*32 + lr of the group.
-    const int my_row = row0 + rb * 32 + lr;
-    const int my_tok = my_row / G;
+    // This wave's row block and this lane's row.
+    const int brow0 = row0 + 32 * rb;
+    const bool block_active = brow0 < nrows;
+    const int my_row = brow0 + lr;
     const bool row_valid = my_row < nrows;
+    const int my_tok = my_row / G;
     const int my_head = g * G + my_row % G;
-    const KeyRange mine = visible_range(my_tok + off, sk, p.causal, p.window_left, p.window_right);
+    KeyRange mine = visible_range(my_tok + off, sk, p.causal, p.window_left, p.window_right);
+    if (!row_valid) {
+        mine.lo = 1;
+        mine.hi = 0;
+    }
 
     const long long q_tok_stride = (long long)p.heads_q * DQK;
     const long long kv_tok_stride = (long long)p.heads_kv * DQK;
 
+    // Q^T slice as the B operand: lane holds row my_row, channels
+    // 288*ch + 16*ks + 8*lh .. +7. Kept in accumulation registers: the MFMAs
+    // read their B operand from there directly, which leaves the vector
+    // registers to the accumulators and to LDS reads in flight.
     bf16x8_t qreg[KSTEPS];
     {
-        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (long long)(q_start + my_tok) * q_tok_stride +
-                             (long long)my_head * DQK + lh * 8;
+        const uint16_t* qp = static_cast<const uint16_t*>(p.q) + (long long)(q_start + (row_valid ? my_tok : 0)) * q_tok_stride +
+                             (long long)my_head * DQK + 288 * ch + lh * 8;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             u32x4_t v = {0u, 0u, 0u, 0u};
             if (row_valid) v = load_u32x4(qp + ks * 16);
             qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
+            asm volatile("" : "+a"(qreg[ks]));
         }
     }
 
-    // K operand reads: row kb*32 + lr, chunk ks*2 + lh -> byte offset
-    // row*ROWB + (ks/4)*128 + kx[ks%4].
-    const int f_lr = swz(lr & 15);
+    // K operand (A of S^T = K Q^T): key lr, logical chunk 36*ch + 2*ks + lh,
+    // at byte kx[ks % 4] + 128*(ks / 4) (adding 8 to a chunk index commutes
+    // with the swizzle, which only touches its low three bits).
     uint32_t kx[4];
+    {
+        const int f = swz(lr);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kx[j] = (uint32_t)((kb * 32 + lr) * ROWB + (((j * 2 + lh) ^ f_lr) << 4));
-    // V^T operand (transposing reads): 16-lane group gq, lane i reads key row
-    // 8*(gq/2) + 4*hi + i/4 of a 16-key step, channels w*128 + db*32 + (gq%2)*16 + 4*(i%4).
+        for (int m = 0; m < 4; ++m) kx[m] = (uint32_t)(lr * ROWB + (((36 * ch + 2 * m + lh) ^ f) << 4));
+    }
+    // V^T operand (A of O^T = V^T P^T), two transposing reads per 32 channels
+    // and 16 keys: 16-lane group gq, lane i reads key 8*which + 4*(gq/2) + i/4
+    // of the 16-key step, channels 256*ch + 32*cb + 16*(gq%2) + 4*(i%4) .. +3,
+    // i.e. logical chunk 32*ch + 4*cb + 2*(gq%2) + (i%4)/2, at byte
+    // vx[which][cb % 2] + 128*(cb / 2) + 16*ROWB*h for key step h.
     uint32_t vx[2][2];
     {
         const int gq = lane >> 4;
         const int i = lane & 15;
-        const int cl = (gq & 1) * 2 + ((i & 3) >> 1);
 #pragma unroll
-        for (int hi2 = 0; hi2 < 2; ++hi2) {
-            const int rowl = 8 * (gq >> 1) + 4 * hi2 + (i >> 2);
-            const int fw = swz(rowl);
+        for (int which = 0; which < 2; ++which) {
+            const int key = 8 * which + 4 * (gq >> 1) + (i >> 2);
+            const int f = swz(key);
 #pragma unroll
-            for (int d1 = 0; d1 < 2; ++d1)
-                vx[hi2][d1] = (uint32_t)(rowl * ROWB + ((w * 16 + ((d1 * 4 + cl) ^ fw)) << 4) + (i & 1) * 8);
+            for (int c2 = 0; c2 < 2; ++c2)
+                vx[which][c2] = (uint32_t)(key * ROWB + (((32 * ch + 4 * c2 + 2 * (gq & 1) + ((i & 3) >> 1)) ^ f) << 4) +
+                                           (i & 1) * 8);
         }
     }
-    // Global -> LDS: chunk position P = n*256 + tid of the tile.
-    uint32_t goff[LOADS];
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
+    // Global -> LDS: 16-byte chunk P = n*256 + tid of a tile is row P/72,
+    // physical chunk P%72, which holds logical chunk (P%72) ^ swz(row).
+    auto goff = [&](int n) __attribute__((always_inline)) -> uint32_t {
         const int P = n * NTHREADS + tid;
         const int row = P / CPR;
-        const int c = (P % CPR) ^ swz(row & 15);
-        goff[n] = (uint32_t)(((long long)row * kv_tok_stride + c * 8) * 2);
-    }
+        const int c = (P % CPR) ^ swz(row);
+        return (uint32_t)(row * (int)(kv_tok_stride * 2) + c * 16);
+    };
     const uint16_t* KVseg = static_cast<const uint16_t*>(p.kv) + (long long)k_start * kv_tok_stride + (long long)g * DQK;
-    auto issue_tile = [&](int kt, int buf) {
+    // Tiles past the key range are issued too, as loads of zero bytes (a
+    // buffer resource of size 0 returns zeros without touching memory), so
+    // every step has the same number of loads in flight behind it.
+    auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) {
         long long bytes = (long long)(sk - kt - 1) * kv_tok_stride * 2 + DQK * 2;
+        if (kt >= sk) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(KVseg + (long long)kt * kv_tok_stride, (uint32_t)bytes);
 #pragma unroll
-        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, sKV + buf * TILEB + (n * NTHREADS + w * 64) * 16, goff[n]);
+        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, stage + (n * NTHREADS + w * 64) * 16, goff(n));
     };
 
-    // O^T accumulators: channel block db (32 channels at w*128 + db*32), row block rr.
-    f32x16_t acc[4][2];
+    // O^T accumulators: channel block cb (channels 256*ch + 32*cb + ...), column lr.
+    f32x16_t acc[CBLK];
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-        acc[db][0] = f32x16_t{};
-        acc[db][1] = f32x16_t{};
-    }
+    for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16_t{};
     float m_run = -INFINITY;  // running max of row my_row, log2 units (may trail the true max by <= 8)
     float l_part = 0.0f;      // running sum over this lane's keys
-    const float c_exp = kCap ? 1.0f : p.x_mul;
+
+    // Partial S^T over this wave's channel half.
+    auto qk_tile = [&](const char* tile) __attribute__((always_inline)) -> f32x16_t {
+        uint32_t kxl[4] = {kx[0], kx[1], kx[2], kx[3]};
+        asm volatile("" : "+v"(kxl[0]), "+v"(kxl[1]), "+v"(kxl[2]), "+v"(kxl[3]));
+        f32x16_t s = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_read16(tile + kxl[ks & 3] + 128 * (ks >> 2)));
+            s = mfma32x32x16(a, qreg[ks], s);
+        }
+        // Schedule: the LDS reads run KQ_AHEAD steps ahead of the MFMAs, and
+        // up to 6 vector-ALU instructions (the softmax of the previous tile)
+        // follow each MFMA.
+        constexpr int KQ_AHEAD = 6;
+        __builtin_amdgcn_sched_group_barrier(0x100, KQ_AHEAD, 0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS - KQ_AHEAD; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KQ_AHEAD; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        }
+        return s;
+    };
+    // Keys this lane's row may use: its own visible range cut to the split,
+    // as key_lo + [0, key_span] (an empty range becomes one no key reaches).
+    int key_lo = max(mine.lo, lo);
+    int key_span = min(mine.hi, hi) - key_lo;
+    if (key_span < 0) {
+        key_lo = 0x40000000;
+        key_span = 0;
+    }
+    // The partial scores of the next tile (MFMAs) interleaved with the
+    // softmax of the current one (vector ALU): after each MFMA one slice of
+    // the softmax, fenced so that the compiler keeps the interleave (the
+    // MFMA runs while the slice issues). s_cur: this wave's partial scores of
+    // the current tile; the partner's are added here. Same arithmetic as
+    // softmax_tile.
+    auto qk_softmax = [&](const char* tile, const f32x16_t& s_cur, int kt, uint32_t (&pk)[8], float& alpha)
+        __attribute__((always_inline)) -> f32x16_t {
+        uint32_t kxl[4] = {kx[0], kx[1], kx[2], kx[3]};
+        asm volatile("" : "+v"(kxl[0]), "+v"(kxl[1]), "+v"(kxl[2]), "+v"(kxl[3]));
+        constexpr int AHEAD = 6;  // K reads in flight ahead of their MFMA
+        bf16x8_t kr[KSTEPS];
+        f32x4_t po[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) po[q4] = sS[w ^ 2][q4][lane];
+#pragma unroll
+        for (int ks = 0; ks < AHEAD; ++ks)
+            kr[ks] = __builtin_bit_cast(bf16x8_t, lds_read16(tile + kxl[ks & 3] + 128 * (ks >> 2)));
+        f32x16_t sn = f32x16_t{};
+        f32x16_t x = s_cur;
+        float mt = -INFINITY, mt_pair = -INFINITY, nb = 0.0f, psum = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            if (ks + AHEAD < KSTEPS)
+                kr[ks + AHEAD] = __builtin_bit_cast(
+                    bf16x8_t, lds_read16(tile + kxl[(ks + AHEAD) & 3] + 128 * ((ks + AHEAD) >> 2)));
+            sn = mfma32x32x16(kr[ks], qreg[ks], sn);
+            if (ks >= 2 && ks < 10) {  // logits, mask and max of elements 2(ks-2), 2(ks-2)+1
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int r = 2 * (ks - 2) + e;
+                    float v = x[r] + po[r >> 2][r & 3];
+                    v = kCap ? score_to_logit<true>(v, p.x_mul, p.cap_mul, p.cap_out) : v * p.x_mul;
+                    const int key = kt + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    v = ((unsigned)(key - key_lo) <= (unsigned)key_span) ? v : -INFINITY;
+                    x[r] = v;
+                    mt = fmaxf(mt, v);
+                }
+            }
+            if (ks == 10) mt_pair = __shfl_xor(mt, 32);
+            if (ks == 12) {
+                mt = fmaxf(mt, mt_pair);
+                const bool grow = mt > m_run + kLazyRescale;
+                const float m_new = grow ? mt : m_run;
+                alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
+                m_run = m_new;
+                nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+            }
+            if (ks >= 13) {  // exp2 and packing, 4 or 3 elements per slice
+                constexpr int kFirst[5] = {0, 4, 6, 10, 12};
+                constexpr int kCount[5] = {4, 2, 4, 2, 4};
+                const int i0 = kFirst[ks - 13];
+#pragma unroll
+                for (int e = 0; e < kCount[ks - 13]; e += 2) {
+                    const int r = i0 + e;
+                    const float p0 = fast_exp2(x[r] + nb);
+                    const float p1 = fast_exp2(x[r + 1] + nb);
+                    psum += p0 + p1;
+                    pk[r >> 1] = pack_bf16x2(p0, p1);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_part = l_part * alpha + psum;
+        return sn;
+    };
+    // O^T += V^T P^T over the tile's two 16-key steps.
+    auto pv_tile = [&](const char* tile, const uint32_t (&pk)[8]) __attribute__((always_inline)) {
+        uint32_t vxl[4] = {vx[0][0], vx[0][1], vx[1][0], vx[1][1]};
+        asm volatile("" : "+v"(vxl[0]), "+v"(vxl[1]), "+v"(vxl[2]), "+v"(vxl[3]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4_t pv = {pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pv);
+#pragma unroll
+            for (int cb = 0; cb < CBLK; ++cb) {
+                const char* base = tile + 16 * ROWB * h + 128 * (cb >> 1);
+                const u32x2_t r0 = lds_read_tr16(base + vxl[cb & 1]);
+                const u32x2_t r1 = lds_read_tr16(base + vxl[2 + (cb & 1)]);
+                const u32x4_t av = {r0[0], r0[1], r1[0], r1[1]};
+                acc[cb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), pb, acc[cb]);
+            }
+        }
+        // Schedule: the transposing reads run PV_AHEAD MFMAs ahead.
+        constexpr int PV_AHEAD = 4;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV_AHEAD, 0);
+#pragma unroll
+        for (int m = 0; m < 2 * CBLK - PV_AHEAD; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD, 0);
+    };
 
     if (lo <= hi) {
         const int kt0 = lo & ~(BN - 1);
         const int ntiles = (hi - kt0) / BN + 1;
-        issue_tile(kt0, 0);
-        wait_vmem();
-        __syncthreads();
-        for (int it = 0; it < ntiles; ++it) {
-            const int kt = kt0 + it * BN;
-            const int buf = it & 1;
-            if (it + 1 < ntiles) issue_tile(kt + BN, buf ^ 1);
-            const char* tile = sKV + buf * TILEB;
-            const bool full = kt >= last.lo && kt + BN - 1 <= first.hi && kt + BN - 1 <= hi && kt >= lo;
-
-            // S^T block (32 keys x 32 rows).
-            f32x16_t s = f32x16_t{};
+        // Tile j lives in stage j % 4. Past the end, tiles are issued as
+        // zero-byte loads, so the count of loads behind each wait is fixed.
+        f32x16_t s_mine = f32x16_t{};
+        auto publish = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, load_u32x4(tile + (ks >> 2) * 128 + kx[ks & 3]));
-                s = mfma32x32x16(a, qreg[ks], s);
-            }
-            float mt = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[r];
-                if constexpr (kCap) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
-                if (!full) {
-                    const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    if (key < mine.lo || key > mine.hi || key < lo || key > hi) x = -INFINITY;
-                }
-                s[r] = x;
-                mt = fmaxf(mt, x);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            if (lh == 0) sMax[kb * ROWS + rb * 32 + lr] = mt;
-            lds_barrier();
-            mt = fmaxf(sMax[rb * 32 + lr], sMax[ROWS + rb * 32 + lr]);
-            if constexpr (!kCap) mt *= c_exp;
-            const bool grow = mt > m_run + kLazyRescale;
-            const float m_new = grow ? mt : m_run;
-            const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-            m_run = m_new;
-            l_part *= alpha;
-            const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
-            float psum = 0.0f;
-            uint16_t* prow = &sP[(rb * 32 + lr) * PSTR + kb * 32 + 4 * lh];
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const float p0 = fast_exp2(fmaf(s[4 * rg + 0], c_exp, nb));
-                const float p1 = fast_exp2(fmaf(s[4 * rg + 1], c_exp, nb));
-                const float p2 = fast_exp2(fmaf(s[4 * rg + 2], c_exp, nb));
-                const float p3 = fast_exp2(fmaf(s[4 * rg + 3], c_exp, nb));
-                psum += (p0 + p1) + (p2 + p3);
-                const u32x2_t pk = {pack_bf16x2(p0, p1), pack_bf16x2(p2, p3)};
-                store_u32x2(prow + 8 * rg, pk);
-            }
-            l_part += psum;
-            if (kb == 0 && lh == 0) sAlpha[rb * 32 + lr] = alpha;
-            lds_barrier();
-
-            // O^T += V^T P^T over the tile's 64 keys (4 steps of 16).
-            {
-                const float a0 = sAlpha[lr];
-                const float a1 = sAlpha[32 + lr];
-                if (wave_any(a0 != 1.0f || a1 != 1.0f)) {
-#pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        acc[db][0] *= a0;
-                        acc[db][1] *= a1;
-                    }
-                }
-            }
-            const uint32_t tbase = lds_addr(tile);
-            uint32_t va[8];
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                va[2 * db] = tbase + vx[0][db & 1] + (db >> 1) * 128;
-                va[2 * db + 1] = tbase + vx[1][db & 1] + (db >> 1) * 128;
-            }
-            pv_k4<0>(acc, va, sP, lr, lh);
-            pv_k4<1>(acc, va, sP, lr, lh);
-            pv_k4<2>(acc, va, sP, lr, lh);
-            pv_k4<3>(acc, va, sP, lr, lh);
-            wait_vmem();
-            __syncthreads();
+            for (int q4 = 0; q4 < 4; ++q4)
+                sS[w][q4][lane] = f32x4_t{s_mine[4 * q4], s_mine[4 * q4 + 1], s_mine[4 * q4 + 2], s_mine[4 * q4 + 3]};
+        };
+        issue_tile(kt0, sT0);
+        issue_tile(kt0 + BN, sT1);
+        issue_tile(kt0 + 2 * BN, sT2);
+        asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's loads of tile 0
+        lds_barrier();
+        if (block_active) {
+            s_mine = qk_tile(sT0);
+            publish();
         }
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's loads of tile 1
+        lds_barrier();
+        issue_tile(kt0 + 3 * BN, sT3);
+        // Step j: add the partner's partial scores of tile j; compute this
+        // wave's partial scores of tile j+1 on the MFMAs while the vector ALU
+        // runs the softmax of tile j; barrier (both partials of tile j read);
+        // publish the partial of tile j+1; P V of tile j; wait for this wave's
+        // loads of tile j+2 (tile j+3 may still run: 9 loads); barrier (tile
+        // j+2 landed, partials of tile j+1 published, tile j consumed); load
+        // tile j+4 into the stage of tile j. Tiles j+2 and j+3 stream in
+        // during the step.
+        auto step = [&](auto stage_tag, int j) __attribute__((always_inline)) {
+            constexpr int S = decltype(stage_tag)::value;
+            char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : S == 2 ? sT2 : sT3;
+            char* const nxt = S == 0 ? sT1 : S == 1 ? sT2 : S == 2 ? sT3 : sT0;
+            uint32_t pk[8];
+            float alpha = 1.0f;
+            if (block_active) {
+                // On the last step this reads a finished (zero-filled) tile;
+                // the result is not used.
+                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha);
+            }
+            lds_barrier();
+            if (block_active) {
+                if (j + 1 < ntiles) publish();
+                if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+                    for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
+                }
+                pv_tile(cur, pk);
+            }
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            lds_barrier();
+            issue_tile(kt0 + (j + 4) * BN, cur);
+        };
+        static_assert(LOADS == 9, "the vmcnt counts above assume 9 loads per tile");
+        using st0 = std::integral_constant<int, 0>;
+        using st1 = std::integral_constant<int, 1>;
+        using st2 = std::integral_constant<int, 2>;
+        using st3 = std::integral_constant<int, 3>;
+        int j = 0;
+        for (; j + STAGES <= ntiles; j += STAGES) {
+            step(st0{}, j);
+            step(st1{}, j + 1);
+            step(st2{}, j + 2);
+            step(st3{}, j + 3);
+        }
+        if (j < ntiles) step(st0{}, j);
+        if (j + 1 < ntiles) step(st1{}, j + 1);
+        if (j + 2 < ntiles) step(st2{}, j + 2);
+        // Drain the look-ahead loads before the work group's LDS is released.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 
-    // Partial (m, l, acc) of this split.
-    const float l_wave = l_part + __shfl_xor(l_part, 32);
-    __syncthreads();
-    if (lh == 0) sSum[kb * ROWS + rb * 32 + lr] = l_wave;
-    if (kb == 0 && lh == 0) sMax[rb * 32 + lr] = m_run;
-    __syncthreads();
+    // Partial (m, l, acc) of this split: row 32*rb + lr of the group, channels
+    // 256*ch + 32*cb + 8*(r/4) + 4*lh + r%4.
     const long long pidx = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits + sp;
-    float* pacc = p.part_acc + pidx * ROWS * DV;
+    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const int grow_idx = 32 * rb + lr;
+    float* pacc = p.part_acc + (pidx * ROWS + grow_idx) * DV + 256 * ch + 4 * lh;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int row = rr * 32 + lr;
+    for (int cb = 0; cb < CBLK; ++cb)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-#pragma unroll
-            for (int rg = 0; rg < 4; ++rg) {
-                const int d = w * 128 + db * 32 + 8 * rg + 4 * lh;
-                const f32x4_t v = {acc[db][rr][4 * rg], acc[db][rr][4 * rg + 1], acc[db][rr][4 * rg + 2],
-                                   acc[db][rr][4 * rg + 3]};
-                *reinterpret_cast<f32x4_t*>(pacc + (long long)row * DV + d) = v;
-            }
-        }
-    }
-    if (tid < ROWS) {
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(pacc + 32 * cb + 8 * q4) =
+                f32x4_t{acc[cb][4 * q4], acc[cb][4 * q4 + 1], acc[cb][4 * q4 + 2], acc[cb][4 * q4 + 3]};
+    if (ch == 0 && lh == 0) {
         float* pml = p.part_ml + pidx * 2 * ROWS;
-        pml[tid] = sMax[tid];
-        pml[ROWS + tid] = sSum[tid] + sSum[ROWS + tid];
+        pml[grow_idx] = m_run;
+        pml[ROWS + grow_idx] = l_row;
     }
 }
 
@@ -360,26 +480,15 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
 
 }  // namespace
 
-size_t decode_split_lds_bytes() { return 2 * TILEB + ROWS * PSTR * 2 + 5 * ROWS * sizeof(float); }
-
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream) {
     const long long units = (long long)p.batch * p.heads_kv * p.m_groups;
     if (units <= 0) return hipSuccess;
     const long long grid_split = units * p.splits;
     if (grid_split > 0x7fffffffLL || units * (ROWS / CROWS) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const size_t lds = decode_split_lds_bytes();
-    // Opt in to more than 64 KB of dynamic LDS (once per kernel instance).
-    static const hipError_t attr_cap = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_split_kernel<true>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    static const hipError_t attr_plain = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_split_kernel<false>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (p.softcap > 0.0f) {
-        if (attr_cap != hipSuccess) return attr_cap;
-        hipLaunchKernelGGL((decode_split_kernel<true>), dim3((unsigned)grid_split), dim3(NTHREADS), lds, stream, p);
-    } else {
-        if (attr_plain != hipSuccess) return attr_plain;
-        hipLaunchKernelGGL((decode_split_kernel<false>), dim3((unsigned)grid_split), dim3(NTHREADS), lds, stream, p);
-    }
+    if (p.softcap > 0.0f)
+        hipLaunchKernelGGL((decode_split_kernel<true>), dim3((unsigned)grid_split), dim3(NTHREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<false>), dim3((unsigned)grid_split), dim3(NTHREADS), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(units * (ROWS / CROWS))), dim3(NTHREADS), 0, stream, p);

@@ -90,8 +90,14 @@ void fwd_bf16_kernel(const FwdParams p) {
     constexpr int TILEB = BN * ROWB;           // bytes per K or V tile
     constexpr int LOADS = TILEB / (16 * NTHREADS);  // 16-byte loads per thread per tile
 
-    __shared__ __attribute__((aligned(TILEB))) char sK[2][TILEB];
-    __shared__ __attribute__((aligned(TILEB))) char sV[2][TILEB];
+    // Four separate LDS objects rather than two arrays of two: reads of one
+    // buffer may then proceed while the buffer loads into another are in
+    // flight (the compiler waits for in-flight LDS-bound loads only before
+    // reads of the object they write).
+    __shared__ __attribute__((aligned(TILEB))) char sK0[TILEB];
+    __shared__ __attribute__((aligned(TILEB))) char sK1[TILEB];
+    __shared__ __attribute__((aligned(TILEB))) char sV0[TILEB];
+    __shared__ __attribute__((aligned(TILEB))) char sV1[TILEB];
 
     const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (item.b < 0) return;
@@ -203,13 +209,16 @@ void fwd_bf16_kernel(const FwdParams p) {
     auto qk = [&](f32x16_t (&s)[2], const char* kt_lds) {
         s[0] = f32x16_t{};
         s[1] = f32x16_t{};
-        const uint32_t kb0 = lds_addr(kt_lds) + kx;
+        // Recompute the per-step offsets in each tile instead of keeping all
+        // of them live across the loop (registers are the scarce resource).
+        uint32_t kxl = kx;
+        asm volatile("" : "+v"(kxl));
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            const uint32_t a0 = kb0 ^ (uint32_t)(ks << 5);
+            const char* a0 = kt_lds + (kxl ^ (uint32_t)(ks << 5));
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_load16(a0 + kb * 32 * ROWB));
+                const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_read16(a0 + kb * 32 * ROWB));
                 s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
             }
         }
@@ -290,56 +299,65 @@ void fwd_bf16_kernel(const FwdParams p) {
         const int kt0 = kv_lo & ~(BN - 1);
         const int ntiles = (kv_hi - kt0) / BN + 1;
         // Prologue: K0, V0, K1 in flight; S and row max of tile 0.
-        issue(Kseg, kt0, sK[0]);
-        issue(Vseg, kt0, sV[0]);
-        if (ntiles > 1) issue(Kseg, kt0 + BN, sK[1]);
+        issue(Kseg, kt0, sK0);
+        issue(Vseg, kt0, sV0);
+        if (ntiles > 1) issue(Kseg, kt0 + BN, sK1);
         wait_vmem();
         __syncthreads();
         f32x16_t sa[2], sb[2];
         float mt_a = -INFINITY, mt_b = -INFINITY;
-        qk(sa, sK[0]);
+        qk(sa, sK0);
         mt_a = tile_full(kt0) ? logits_max(std::false_type{}, sa, kt0) : logits_max(std::true_type{}, sa, kt0);
         lds_barrier();  // every wave is done with K0 before K2 overwrites it
 
-        // Tile j: S_j in s_cur (masked, max mt_cur); K(j+1) and V(j) resident.
-        auto step = [&](auto has_next_tag, int j, f32x16_t (&s_cur)[2], float mt_cur, f32x16_t (&s_next)[2],
-                        float& mt_next) {
+        // Tile j (parity P = j % 2): S_j in s_cur (masked, max mt_cur); K(j+1)
+        // in sK[1-P] and V(j) in sV[P] are resident; K(j+2) goes to sK[P] and
+        // V(j+1) to sV[1-P].
+        auto step = [&](auto has_next_tag, auto parity_tag, int j, f32x16_t (&s_cur)[2], float mt_cur,
+                        f32x16_t (&s_next)[2], float& mt_next) {
             constexpr bool kNext = decltype(has_next_tag)::value;
+            constexpr int P = decltype(parity_tag)::value;
+            char* const k_fill = P ? sK1 : sK0;
+            const char* const k_use = P ? sK0 : sK1;
+            char* const v_fill = P ? sV0 : sV1;
+            const char* const v_use = P ? sV1 : sV0;
             const int kt = kt0 + j * BN;
-            if (j + 2 < ntiles) issue(Kseg, kt + 2 * BN, sK[j & 1]);
-            if (j + 1 < ntiles) issue(Vseg, kt + BN, sV[(j + 1) & 1]);
+            if (j + 2 < ntiles) issue(Kseg, kt + 2 * BN, k_fill);
+            if (j + 1 < ntiles) issue(Vseg, kt + BN, v_fill);
             update_max(mt_cur);
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
-                qk(s_next, sK[(j + 1) & 1]);
+                qk(s_next, k_use);
                 exp_tile(s_cur, pk);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
                 if (tile_full(kt + BN)) {
-                    pv(pk, sV[j & 1]);
+                    pv(pk, v_use);
                     mt_next = logits_max(std::false_type{}, s_next, kt + BN);
                 } else {
-                    pv(pk, sV[j & 1]);
+                    pv(pk, v_use);
                     mt_next = logits_max(std::true_type{}, s_next, kt + BN);
                 }
             } else {
                 exp_tile(s_cur, pk);
-                pv(pk, sV[j & 1]);
+                pv(pk, v_use);
             }
             wait_vmem();
             __syncthreads();
         };
+        using even = std::integral_constant<int, 0>;
+        using odd = std::integral_constant<int, 1>;
 
         int j = 0;
         for (; j + 2 < ntiles; j += 2) {
-            step(std::true_type{}, j, sa, mt_a, sb, mt_b);
-            step(std::true_type{}, j + 1, sb, mt_b, sa, mt_a);
+            step(std::true_type{}, even{}, j, sa, mt_a, sb, mt_b);
+            step(std::true_type{}, odd{}, j + 1, sb, mt_b, sa, mt_a);
         }
         if (j + 1 < ntiles) {
-            step(std::true_type{}, j, sa, mt_a, sb, mt_b);
-            step(std::false_type{}, j + 1, sb, mt_b, sa, mt_a);
+            step(std::true_type{}, even{}, j, sa, mt_a, sb, mt_b);
+            step(std::false_type{}, odd{}, j + 1, sb, mt_b, sa, mt_a);
         } else {
-            step(std::false_type{}, j, sa, mt_a, sb, mt_b);
+            step(std::false_type{}, even{}, j, sa, mt_a, sb, mt_b);
         }
     }
 

@@ -88,18 +88,17 @@ int device_cus(int* out) {
     return 0;
 }
 
-constexpr int kDecodeBN = 64;  // keys per decode tile (split boundaries are tile aligned)
 constexpr int kMaxSplits = 64;
 
 // Split plan: aim for about one work group per compute unit (the split kernel
-// holds a 74 KB K/V tile and a P tile in LDS, one group per CU).
+// keeps four 36 KB latent tiles in LDS, one group per CU).
 int plan_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, int heads_kv, int requested,
                 int* err) {
     *err = 0;
     const int group = heads_q / heads_kv;
     const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kDecodeRows - 1) / mxfa::kDecodeRows;
     const long long units = (long long)batch * heads_kv * m_groups;
-    const int tiles = (max_seqlen_k + kDecodeBN - 1) / kDecodeBN;
+    const int tiles = (max_seqlen_k + mxfa::kDecodeTile - 1) / mxfa::kDecodeTile;
     if (requested > 0) return requested;
     int cus = 0;
     int e = device_cus(&cus);

@@ -88,6 +88,14 @@ MXFA_DEV f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// D = A * B + C for a 16x16 tile with a 32-deep contraction, bf16 inputs,
+// fp32 accumulate. Lane l holds A row (l % 16) and B column (l % 16), eight
+// contraction elements each (the same eight for A and B); D: lane l,
+// register r -> column l % 16, row 4 * (l / 16) + r.
+MXFA_DEV f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- memory
 
 MXFA_DEV u32x4_t load_u32x4(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
@@ -176,11 +184,77 @@ MXFA_DEV void lds_read_tr16_x8(u32x2_t (&r)[8], const uint32_t (&a)[8]) {
 }
 
 // 16-byte LDS read at a byte address (ds_read_b128).
+// Sixteen transposing reads: address a[i] at offsets OFF0, OFF1, OFF2, OFF3
+// for i = 0..3 (read 4*k + i uses offset k); waits for all of them before the
+// block ends.
+template <int OFF0, int OFF1, int OFF2, int OFF3>
+MXFA_DEV void lds_read_tr16_4x4(u32x2_t (&r)[16], const uint32_t (&a)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%20\n\t"
+        "ds_read_b64_tr_b16 %4, %16 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %5, %17 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %6, %18 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%22\n\t"
+        "ds_read_b64_tr_b16 %12, %16 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %13, %17 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %14, %18 offset:%23\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(OFF0), "i"(OFF1), "i"(OFF2), "i"(OFF3)
+        : "memory");
+}
+
+// 16-byte LDS read through a pointer into a __shared__ object (keeps the
+// object's identity, so the read waits only for LDS-bound loads into it).
+// Sixteen transposing reads: addresses a[0..7] at offset OFF0, then a[0..7]
+// at offset OFF1; waits for all of them before the block ends.
+template <int OFF0, int OFF1>
+MXFA_DEV void lds_read_tr16_x16(u32x2_t (&r)[16], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]),
+          "=&v"(r[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]), "i"(OFF0), "i"(OFF1)
+        : "memory");
+}
+
+MXFA_DEV u32x4_t lds_read16(const void* p) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(to_lds(const_cast<void*>(p)));
+}
+
 MXFA_DEV u32x4_t lds_load16(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((size_t)addr);
 }
 
 MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+
 
 // ---------------------------------------------------------------- work mapping
 

@@ -70,5 +70,7 @@ hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 
 // Rows of one decode work group: (query token, head-in-group) pairs.
 constexpr int kDecodeRows = 64;
+// Keys per decode tile; split boundaries are multiples of it.
+constexpr int kDecodeTile = 32;
 
 }  // namespace mxfa
