@@ -20,6 +20,14 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W,
 --workloads a,b,... (default: causal_prefill_bf16,mla_decode_bf16; "all"
 adds the other configurations as extra lines in ``extra``),
 --no-cpu-baseline, --cpu-seconds S.
+
+Traffic counters: run the bench under ``rocprofv3 --pmc FETCH_SIZE`` and,
+separately, ``--pmc WRITE_SIZE`` with ``--copy-probe-mb N`` (a device copy of
+N MiB after the workloads, whose counter readings calibrate the counters),
+then ``python bench.py --pmc-summarize FETCH_CSV WRITE_CSV --copy-probe-mb N``
+writes profiles/pmc_traffic.json: measured HBM bytes per launch for each
+kernel, tagged with the hash of the kernel's source (ignored once the source
+changes).
 """
 from __future__ import annotations
 
@@ -85,6 +93,66 @@ def work_of(w, inp):
 def source_sha(name):
     with open(os.path.join(ROOT, KERNEL_SOURCES[name]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# rocprofv3 kernel names of each kernel family (one launch of mxfa_decode_splitkv
+# is one split kernel plus one combine kernel).
+PMC_KERNELS = {
+    "fwd_bf16": ("fwd_bf16_kernel<128, 0>",),
+    "decode_mla": ("decode_split_kernel<false>", "decode_combine_kernel"),
+}
+COPY_KERNEL_MARKERS = ("copyBuffer", "copy_kernel", "CopyKernel")
+
+
+def _pmc_readings(csv_path, counter):
+    """Counter values (KiB) of every dispatch, by kernel name."""
+    import csv
+
+    out = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def pmc_summarize(fetch_csv, write_csv, copy_mb):
+    """Turn two rocprofv3 PMC runs into bytes per launch per kernel family."""
+    fetch_all = _pmc_readings(fetch_csv, "FETCH_SIZE")
+    write_all = _pmc_readings(write_csv, "WRITE_SIZE")
+    fetch = {k: sum(v) / len(v) for k, v in fetch_all.items()}
+    write = {k: sum(v) / len(v) for k, v in write_all.items()}
+
+    def copy_reading(readings):
+        cands = [x for k, v in readings.items() if any(m in k for m in COPY_KERNEL_MARKERS) for x in v]
+        if not cands:
+            raise SystemExit("no copy kernel in the counter file; run with --copy-probe-mb")
+        return max(cands)  # the probe copy is the largest copy dispatch in the run
+
+    copy_bytes = copy_mb * 2 ** 20
+    f_scale = copy_bytes / (copy_reading(fetch_all) * 1024.0)
+    w_scale = copy_bytes / (copy_reading(write_all) * 1024.0)
+    out = {"_calibration": {"copy_bytes": copy_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
+                            "note": "bytes = counter KiB * 1024 * scale; scale = copy bytes / copy reading"}}
+    for fam, names in PMC_KERNELS.items():
+        fb = wb = 0.0
+        raw = {}
+        for n in names:
+            fk = [v for k, v in fetch.items() if n in k]
+            wk = [v for k, v in write.items() if n in k]
+            if not fk or not wk:
+                break
+            raw[n] = {"FETCH_SIZE_KiB": fk[0], "WRITE_SIZE_KiB": wk[0]}
+            fb += fk[0] * 1024.0 * f_scale
+            wb += wk[0] * 1024.0 * w_scale
+        else:
+            out[fam] = {"source_sha": source_sha(fam), "bytes_per_launch": round(fb + wb),
+                        "fetch_bytes": round(fb), "write_bytes": round(wb), "raw": raw}
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def load_traffic(kernel):
@@ -248,7 +316,14 @@ def main():
     ap.add_argument("--workloads", default=f"{PRIMARY},{DECODE}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mb", type=int, default=0)
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.pmc_summarize:
+        if args.copy_probe_mb <= 0:
+            raise SystemExit("--pmc-summarize needs --copy-probe-mb (the size of the calibration copy)")
+        pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], args.copy_probe_mb)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
               "(the multi-GPU sharding is a design, see DESIGN.md)", file=sys.stderr)
@@ -286,6 +361,17 @@ def main():
               file=sys.stderr, flush=True)
         del r
         torch.cuda.empty_cache()
+
+    if args.copy_probe_mb > 0:
+        # Calibration copy for the traffic counters: reads and writes exactly
+        # copy_probe_mb MiB (not part of the JSON line).
+        src = torch.empty(args.copy_probe_mb * 2 ** 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy probe: {args.copy_probe_mb} MiB x 3", file=sys.stderr, flush=True)
+        del src, dst
 
     p = results[PRIMARY]
     w = __import__("workloads").get(PRIMARY)
