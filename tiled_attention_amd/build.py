@@ -36,12 +36,13 @@ def compile_flags() -> list:
             "-I", INCLUDE, "-I", CSRC]
 
 
-# Extra flags per source. The decode kernel keeps 128 fp32 accumulators per
-# lane live next to its Q^T operand; left to its heuristics the compiler
-# moves them between VGPRs and AGPRs around every tile, so its MFMAs are
-# pinned to the VGPR form.
+# Extra flags per source. The decode and bf16 forward kernels keep 128 fp32
+# accumulators per lane live next to a Q^T operand held in AGPRs; left to its
+# heuristics the compiler moves the accumulators between VGPRs and AGPRs
+# around every tile, so their MFMAs are pinned to the VGPR form.
 FILE_FLAGS = {
     "decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -178,15 +178,17 @@ void decode_split_kernel(const DecodeParams p) {
     const uint16_t* KVseg = static_cast<const uint16_t*>(p.kv) + (long long)k_start * kv_tok_stride + (long long)g * DQK;
     // Tiles past the key range are issued too, as loads of zero bytes (a
     // buffer resource of size 0 returns zeros without touching memory), so
-    // every step has the same number of loads in flight behind it.
-    auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) {
+    // every step has the same number of loads in flight behind it. A tile's
+    // loads may be issued in parts (loads [n0, n1)).
+    auto issue_part = [&](int kt, char* stage, int n0, int n1) __attribute__((always_inline)) {
         long long bytes = (long long)(sk - kt - 1) * kv_tok_stride * 2 + DQK * 2;
         if (kt >= sk) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
         const __amdgpu_buffer_rsrc_t r = make_rsrc(KVseg + (long long)kt * kv_tok_stride, (uint32_t)bytes);
 #pragma unroll
-        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, stage + (n * NTHREADS + w * 64) * 16, goff(n));
+        for (int n = n0; n < n1; ++n) buffer_load_lds16(r, stage + (n * NTHREADS + w * 64) * 16, goff(n));
     };
+    auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) { issue_part(kt, stage, 0, LOADS); };
 
     // O^T accumulators: channel block cb (channels 256*ch + 32*cb + ...), column lr.
     f32x16_t acc[CBLK];
@@ -237,8 +239,8 @@ void decode_split_kernel(const DecodeParams p) {
     // MFMA runs while the slice issues). s_cur: this wave's partial scores of
     // the current tile; the partner's are added here. Same arithmetic as
     // softmax_tile.
-    auto qk_softmax = [&](const char* tile, const f32x16_t& s_cur, int kt, uint32_t (&pk)[8], float& alpha)
-        __attribute__((always_inline)) -> f32x16_t {
+    auto qk_softmax = [&](const char* tile, const f32x16_t& s_cur, int kt, uint32_t (&pk)[8], float& alpha,
+                          auto&& mid_hook) __attribute__((always_inline)) -> f32x16_t {
         uint32_t kxl[4] = {kx[0], kx[1], kx[2], kx[3]};
         asm volatile("" : "+v"(kxl[0]), "+v"(kxl[1]), "+v"(kxl[2]), "+v"(kxl[3]));
         constexpr int AHEAD = 6;  // K reads in flight ahead of their MFMA
@@ -272,6 +274,7 @@ void decode_split_kernel(const DecodeParams p) {
                 }
             }
             if (ks == 10) mt_pair = __shfl_xor(mt, 32);
+            if (ks == 6) mid_hook();
             if (ks == 12) {
                 mt = fmaxf(mt, mt_pair);
                 const bool grow = mt > m_run + kLazyRescale;
@@ -348,27 +351,34 @@ void decode_split_kernel(const DecodeParams p) {
         }
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's loads of tile 1
         lds_barrier();
-        issue_tile(kt0 + 3 * BN, sT3);
         // Step j: add the partner's partial scores of tile j; compute this
         // wave's partial scores of tile j+1 on the MFMAs while the vector ALU
         // runs the softmax of tile j; barrier (both partials of tile j read);
         // publish the partial of tile j+1; P V of tile j; wait for this wave's
         // loads of tile j+2 (tile j+3 may still run: 9 loads); barrier (tile
-        // j+2 landed, partials of tile j+1 published, tile j consumed); load
-        // tile j+4 into the stage of tile j. Tiles j+2 and j+3 stream in
-        // during the step.
+        // j+2 landed, partials of tile j+1 published, tile j consumed). The
+        // loads of tile j+3 go into the stage of tile j-1 (consumed before
+        // the previous step's closing barrier) in three parts spread over the
+        // step, so that their issue overlaps the MFMAs.
         auto step = [&](auto stage_tag, int j) __attribute__((always_inline)) {
             constexpr int S = decltype(stage_tag)::value;
             char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : S == 2 ? sT2 : sT3;
             char* const nxt = S == 0 ? sT1 : S == 1 ? sT2 : S == 2 ? sT3 : sT0;
+            char* const prv = S == 0 ? sT3 : S == 1 ? sT0 : S == 2 ? sT1 : sT2;
+            const int kt_fill = kt0 + (j + 3) * BN;  // tile j+3 -> the stage of tile j-1
             uint32_t pk[8];
             float alpha = 1.0f;
+            issue_part(kt_fill, prv, 0, 3);
             if (block_active) {
                 // On the last step this reads a finished (zero-filled) tile;
                 // the result is not used.
-                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha);
+                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha,
+                                    [&]() __attribute__((always_inline)) { issue_part(kt_fill, prv, 3, 6); });
+            } else {
+                issue_part(kt_fill, prv, 3, 6);
             }
             lds_barrier();
+            issue_part(kt_fill, prv, 6, LOADS);
             if (block_active) {
                 if (j + 1 < ntiles) publish();
                 if (wave_any(alpha != 1.0f)) {
@@ -379,7 +389,6 @@ void decode_split_kernel(const DecodeParams p) {
             }
             asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
             lds_barrier();
-            issue_tile(kt0 + (j + 4) * BN, cur);
         };
         static_assert(LOADS == 9, "the vmcnt counts above assume 9 loads per tile");
         using st0 = std::integral_constant<int, 0>;

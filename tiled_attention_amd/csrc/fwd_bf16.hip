@@ -99,7 +99,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     __shared__ __attribute__((aligned(TILEB))) char sV0[TILEB];
     __shared__ __attribute__((aligned(TILEB))) char sV1[TILEB];
 
-    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
+    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles, p.xcd_cus);
     if (item.b < 0) return;
     const int b = item.b;
     const int h = item.h;
@@ -191,10 +191,16 @@ void fwd_bf16_kernel(const FwdParams p) {
         long long bytes = (long long)(sk - kt - 1) * kv_tok * 2 + D * 2;
         return (uint32_t)(bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
     };
-    auto issue = [&](const uint16_t* seg, int kt, char* tile) {
+    // Loads [n0, n1) of a tile (a tile is LOADS loads per thread); issuing a
+    // tile in parts spread over a step keeps the CU's vector-memory path from
+    // stalling every wave at once.
+    auto issue_part = [&](const uint16_t* seg, int kt, char* tile, int n0, int n1) __attribute__((always_inline)) {
         const __amdgpu_buffer_rsrc_t r = make_rsrc(seg + (long long)kt * kv_tok, tile_bytes(kt));
 #pragma unroll
-        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, tile + (n * NTHREADS + wave * 64) * 16, goff, n * gstep);
+        for (int n = n0; n < n1; ++n) buffer_load_lds16(r, tile + (n * NTHREADS + wave * 64) * 16, goff, n * gstep);
+    };
+    auto issue = [&](const uint16_t* seg, int kt, char* tile) __attribute__((always_inline)) {
+        issue_part(seg, kt, tile, 0, LOADS);
     };
 
     f32x16_t acc[DBLK];
@@ -206,7 +212,7 @@ void fwd_bf16_kernel(const FwdParams p) {
 
     // ---- pipeline pieces
     // S^T = K Q^T for one tile.
-    auto qk = [&](f32x16_t (&s)[2], const char* kt_lds) {
+    auto qk = [&](f32x16_t (&s)[2], const char* kt_lds, auto&& mid_hook) __attribute__((always_inline)) {
         s[0] = f32x16_t{};
         s[1] = f32x16_t{};
         // Recompute the per-step offsets in each tile instead of keeping all
@@ -221,6 +227,7 @@ void fwd_bf16_kernel(const FwdParams p) {
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_read16(a0 + kb * 32 * ROWB));
                 s[kb] = mfma32x32x16(a, qreg[ks], s[kb]);
             }
+            if (ks == KSTEPS / 2 - 1) mid_hook();
         }
     };
     // Logits (raw scores in mode 0), mask, and the tile's row max in log2 units.
@@ -280,7 +287,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         l_part += psum;
     };
     // O^T += V^T P^T for one tile.
-    auto pv = [&](const uint32_t (&pk)[2][8], const char* vt_lds) {
+    auto pv = [&](const uint32_t (&pk)[2][8], const char* vt_lds, auto&& mid_hook) __attribute__((always_inline)) {
         uint32_t va[2 * DBLK];
         const uint32_t v0 = lds_addr(vt_lds) + vx[0];
         const uint32_t v1 = lds_addr(vt_lds) + vx[1];
@@ -291,8 +298,111 @@ void fwd_bf16_kernel(const FwdParams p) {
         }
         pv_step<D, 0, 0>(acc, pk, va);
         pv_step<D, 0, 1>(acc, pk, va);
+        mid_hook();
         pv_step<D, 1, 0>(acc, pk, va);
         pv_step<D, 1, 1>(acc, pk, va);
+    };
+
+    // Phase A, fused: S_{j+1} = K_{j+1} Q^T on the MFMAs while the vector
+    // ALU turns S_j into P_j. After each MFMA one slice of the exponentials
+    // (two elements), fenced so that the compiler keeps the interleave; the K
+    // operand reads run AHEAD MFMAs ahead.
+    auto qk_exp = [&](f32x16_t (&sn)[2], const char* kt_lds, f32x16_t (&sc)[2], uint32_t (&pk)[2][8],
+                      auto&& mid_hook) __attribute__((always_inline)) {
+        constexpr int NM = 2 * KSTEPS;  // MFMAs: m = 2*ks + kb
+        constexpr int EPS = 32 / NM;    // exponentials per slice
+        constexpr int AHEAD = 4;
+        sn[0] = f32x16_t{};
+        sn[1] = f32x16_t{};
+        uint32_t kxl = kx;
+        asm volatile("" : "+v"(kxl));
+        auto rd = [&](int m) __attribute__((always_inline)) {
+            return __builtin_bit_cast(bf16x8_t,
+                                      lds_read16(kt_lds + (kxl ^ (uint32_t)((m >> 1) << 5)) + (m & 1) * 32 * ROWB));
+        };
+        bf16x8_t a[NM];
+#pragma unroll
+        for (int m = 0; m < AHEAD; ++m) a[m] = rd(m);
+        const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+        float psum = 0.0f;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m + AHEAD < NM) a[m + AHEAD] = rd(m + AHEAD);
+            sn[m & 1] = mfma32x32x16(a[m], qreg[m >> 1], sn[m & 1]);
+#pragma unroll
+            for (int e = 0; e < EPS; e += 2) {
+                const int idx = m * EPS + e;
+                const int kb = idx >> 4;
+                const int r = idx & 15;
+                const float p0 = fast_exp2(fmaf(sc[kb][r], c_exp, nb));
+                const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c_exp, nb));
+                pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+                psum += p0 + p1;
+            }
+            if (m == NM / 2 - 1) mid_hook();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        l_part += psum;
+    };
+    // Phase B, fused: O += V_j P_j on the MFMAs while the vector ALU takes
+    // the logits, mask and row max of S_{j+1}, a slice after each MFMA; the
+    // transposing V reads run AHEAD MFMAs ahead.
+    auto pv_max = [&](auto masked_tag, const uint32_t (&pk)[2][8], const char* vt_lds, f32x16_t (&sn)[2], int kt,
+                      auto&& mid_hook) __attribute__((always_inline)) -> float {
+        constexpr bool kMasked = decltype(masked_tag)::value;
+        constexpr int NP = 4 * DBLK;  // MFMAs: n = DBLK*step + db, step = 2*kb + half (16 keys each)
+        constexpr int EPS = 32 / NP;  // score elements per slice
+        constexpr int AHEAD = 4;
+        uint32_t vxl[2] = {vx[0], vx[1]};
+        asm volatile("" : "+v"(vxl[0]), "+v"(vxl[1]));
+        auto rd = [&](int n, int which) __attribute__((always_inline)) {
+            const int st = n / DBLK;
+            const int db = n % DBLK;
+            return lds_read_tr16(vt_lds + st * 16 * ROWB + (vxl[which] ^ (uint32_t)(db << 6)));
+        };
+        u32x2_t r0[NP], r1[NP];
+#pragma unroll
+        for (int n = 0; n < AHEAD; ++n) {
+            r0[n] = rd(n, 0);
+            r1[n] = rd(n, 1);
+        }
+        float mm = -INFINITY;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+            if (n + AHEAD < NP) {
+                r0[n + AHEAD] = rd(n + AHEAD, 0);
+                r1[n + AHEAD] = rd(n + AHEAD, 1);
+            }
+            const int st = n / DBLK;
+            const int db = n % DBLK;
+            const int kb = st >> 1;
+            const int half = st & 1;
+            const u32x4_t av = {r0[n][0], r0[n][1], r1[n][0], r1[n][1]};
+            const u32x4_t pv4 = {pk[kb][4 * half], pk[kb][4 * half + 1], pk[kb][4 * half + 2], pk[kb][4 * half + 3]};
+            acc[db] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, pv4), acc[db]);
+#pragma unroll
+            for (int e = 0; e < EPS; ++e) {
+                const int idx = n * EPS + e;
+                const int skb = idx >> 4;
+                const int r = idx & 15;
+                float x = sn[skb][r];
+                if constexpr (kMode == 1) x = x * p.x_mul;
+                if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
+                if constexpr (kMasked) {
+                    const int key = kt + skb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                    x = (key >= mine.lo && key <= mine.hi) ? x : -INFINITY;
+                }
+                sn[skb][r] = x;
+                mm = fmaxf(mm, x);
+            }
+            if (n == NP / 2 - 1) mid_hook();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mm = fmaxf(mm, __shfl_xor(mm, 32));
+        if constexpr (kMode == 0) mm *= c_exp;
+        return mm;
     };
 
     if (kv_lo <= kv_hi) {
@@ -306,7 +416,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         __syncthreads();
         f32x16_t sa[2], sb[2];
         float mt_a = -INFINITY, mt_b = -INFINITY;
-        qk(sa, sK0);
+        qk(sa, sK0, [] {});
         mt_a = tile_full(kt0) ? logits_max(std::false_type{}, sa, kt0) : logits_max(std::true_type{}, sa, kt0);
         lds_barrier();  // every wave is done with K0 before K2 overwrites it
 
@@ -322,25 +432,33 @@ void fwd_bf16_kernel(const FwdParams p) {
             char* const v_fill = P ? sV0 : sV1;
             const char* const v_use = P ? sV1 : sV0;
             const int kt = kt0 + j * BN;
-            if (j + 2 < ntiles) issue(Kseg, kt + 2 * BN, k_fill);
-            if (j + 1 < ntiles) issue(Vseg, kt + BN, v_fill);
+            // K(j+2) and V(j+1) go out in four parts: before and inside each phase.
+            constexpr int H = LOADS / 2;
+            const bool k_more = j + 2 < ntiles;
+            const bool v_more = j + 1 < ntiles;
+            auto k_second = [&]() __attribute__((always_inline)) {
+                if (k_more) issue_part(Kseg, kt + 2 * BN, k_fill, H, LOADS);
+            };
+            auto v_second = [&]() __attribute__((always_inline)) {
+                if (v_more) issue_part(Vseg, kt + BN, v_fill, H, LOADS);
+            };
+            if (k_more) issue_part(Kseg, kt + 2 * BN, k_fill, 0, H);
             update_max(mt_cur);
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
-                qk(s_next, k_use);
-                exp_tile(s_cur, pk);
+                qk_exp(s_next, k_use, s_cur, pk, k_second);
+                if (v_more) issue_part(Vseg, kt + BN, v_fill, 0, H);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
-                if (tile_full(kt + BN)) {
-                    pv(pk, v_use);
-                    mt_next = logits_max(std::false_type{}, s_next, kt + BN);
-                } else {
-                    pv(pk, v_use);
-                    mt_next = logits_max(std::true_type{}, s_next, kt + BN);
-                }
+                if (tile_full(kt + BN))
+                    mt_next = pv_max(std::false_type{}, pk, v_use, s_next, kt + BN, v_second);
+                else
+                    mt_next = pv_max(std::true_type{}, pk, v_use, s_next, kt + BN, v_second);
             } else {
+                k_second();
                 exp_tile(s_cur, pk);
-                pv(pk, v_use);
+                if (v_more) issue_part(Vseg, kt + BN, v_fill, 0, H);
+                pv(pk, v_use, v_second);
             }
             wait_vmem();
             __syncthreads();

@@ -62,7 +62,12 @@ void fill_scaling(float scale, float softcap, float* x_mul, float* cap_mul, floa
     }
 }
 
-mxfa_status launch_fwd(const mxfa::FwdParams& p, int head_dim, mxfa_dtype dtype, hipStream_t stream) {
+int device_cus(int* out);
+
+mxfa_status launch_fwd(const mxfa::FwdParams& args, int head_dim, mxfa_dtype dtype, hipStream_t stream) {
+    mxfa::FwdParams p = args;
+    int cus = 0;
+    if (device_cus(&cus) == 0 && cus % mxfa::kXcdCount == 0) p.xcd_cus = cus / mxfa::kXcdCount;
     hipError_t e = (dtype == MXFA_BF16) ? mxfa::launch_fwd_bf16(p, head_dim, stream)
                                         : mxfa::launch_fwd_f32(p, head_dim, stream);
     if (e != hipSuccess) return hip_fail(e, "forward kernel launch");

@@ -20,7 +20,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kXcds = kXcdCount;  // MI355X: 8 accelerator complex dies, each with its own L2
 
 #define MXFA_DEV __device__ __forceinline__
 
@@ -265,18 +265,27 @@ MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
 // query heads of one kv group stay on one XCD, where they share K/V in its
 // L2. Each XCD walks its items by q tile from the last (most keys under a
 // causal mask) to the first.
+//
+// Within an XCD the hardware places work groups on its CUs round-robin, so
+// with two groups per CU the n-th and (n + C)-th groups of an XCD (C = CUs per
+// XCD) share a CU for the whole first round. pair_span = C (0: off) mirrors
+// the second half of that round: position n in [C, 2C) takes item 3C - 1 - n,
+// so each CU starts with a long and a short item of the first 2C instead of
+// two similar ones; later positions keep the longest-first order.
 struct WorkItem {
     int b;      // batch / segment, or -1 for a padding workgroup
     int h;      // query head
     int qtile;
 };
 
-MXFA_DEV WorkItem map_workgroup(int id, int batch, int heads_kv, int group, int n_qtiles) {
+MXFA_DEV WorkItem map_workgroup(int id, int batch, int heads_kv, int group, int n_qtiles, int pair_span = 0) {
     const int x = id % kXcds;
-    const int n = id / kXcds;
+    int n = id / kXcds;
     const int groups = batch * heads_kv;
     const int groups_per_xcd = (groups + kXcds - 1) / kXcds;
     const int per_rank = groups_per_xcd * group;
+    if (pair_span > 0 && per_rank * n_qtiles >= 2 * pair_span && n >= pair_span && n < 2 * pair_span)
+        n = 3 * pair_span - 1 - n;
     const int rank = n / per_rank;
     const int rem = n % per_rank;
     const int g = (rem / group) * kXcds + x;

@@ -34,6 +34,7 @@ struct FwdParams {
     float cap_mul;           // cap: 2*log2e*scale/cap
     float cap_out;           // cap: cap*log2e
     int n_qtiles;            // ceil(seqlen_q / BM), set by the launcher
+    int xcd_cus;             // compute units per XCD (pairing of the first dispatch round), 0 = unknown
 };
 
 // One latent-KV split decode.
@@ -67,6 +68,9 @@ struct DecodeParams {
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+
+// Accelerator dies (XCDs) of the device, each with its own L2.
+constexpr int kXcdCount = 8;
 
 // Rows of one decode work group: (query token, head-in-group) pairs.
 constexpr int kDecodeRows = 64;
