@@ -189,6 +189,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     // Bytes from key kt on that hold keys < sk (keys past the end read as zero).
     auto tile_bytes = [&](int kt) -> uint32_t {
         long long bytes = (long long)(sk - kt - 1) * kv_tok * 2 + D * 2;
+        if (kt >= sk) bytes = 0;  // a tile wholly past the end is a zero-byte load
         return (uint32_t)(bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
     };
     // Loads [n0, n1) of a tile (a tile is LOADS loads per thread); issuing a
@@ -411,9 +412,11 @@ void fwd_bf16_kernel(const FwdParams p) {
         // Prologue: K0, V0, K1 in flight; S and row max of tile 0.
         issue(Kseg, kt0, sK0);
         issue(Vseg, kt0, sV0);
-        if (ntiles > 1) issue(Kseg, kt0 + BN, sK1);
-        wait_vmem();
-        __syncthreads();
+        issue(Kseg, kt0 + BN, sK1);  // zero-byte past the end
+        // Q and K0 are all tile 0's scores need (V0 and K1 may still run);
+        // the first step's closing wait covers the rest.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * LOADS) : "memory");
+        lds_barrier();
         f32x16_t sa[2], sb[2];
         float mt_a = -INFINITY, mt_b = -INFINITY;
         qk(sa, sK0, [] {});
