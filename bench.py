@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "fwd_bf16": "tiled_attention_amd/csrc/fwd_bf16.hip",
     "fwd_f32": "tiled_attention_amd/csrc/fwd_f32.hip",
     "decode_mla": "tiled_attention_amd/csrc/decode_mla.hip",
+    "decode_mla_paged": "tiled_attention_amd/csrc/decode_mla.hip",
 }
 
 
@@ -99,7 +100,8 @@ def source_sha(name):
 # is one split kernel plus one combine kernel).
 PMC_KERNELS = {
     "fwd_bf16": ("fwd_bf16_kernel<128, 0>",),
-    "decode_mla": ("decode_split_kernel<false>", "decode_combine_kernel"),
+    "decode_mla": ("decode_split_kernel<false, false>", "decode_combine_kernel"),
+    "decode_mla_paged": ("decode_split_kernel<false, true>", "decode_combine_kernel"),
 }
 COPY_KERNEL_MARKERS = ("copyBuffer", "copy_kernel", "CopyKernel")
 
@@ -178,7 +180,7 @@ class Runner:
         import workloads
 
         self.w = w = workloads.get(name)
-        self.inp = inp = workloads.make_inputs(w)
+        inp = workloads.make_inputs(w)
         dev = torch.device("cuda:0")
         self.pairs, self.flops, self.bytes = work_of(w, inp)
         scale = w.softmax_scale
@@ -199,17 +201,28 @@ class Runner:
                                                    softcap=w.softcap, scale=scale, out=o, lse=lse)
             self.kernel = "fwd_bf16"
         else:
-            q, kv = inp["q"].to(dev), inp["kv"].to(dev)
-            cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
+            q = inp["q"].to(dev)
+            cq = inp["cu_seqlens_q"].to(dev)
             o = torch.empty((q.shape[0], w.heads_q, w.d_v), dtype=q.dtype, device=dev)
             lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device=dev)
             self.splits = mx.mxfa_decode_splitkv_num_splits(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q, w.heads_kv)
             nbytes = mx.mxfa_decode_splitkv_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q,
                                                             w.heads_kv, w.d_v)
             ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            self.call = lambda: mx.mxfa_decode_splitkv(q, kv, cq, ck, w.seqlen_q, w.seqlen_k, head_dim_v=w.d_v,
-                                                       scale=scale, workspace=ws, out=o, lse=lse)
-            self.kernel = "decode_mla"
+            if w.page_size:
+                cache = inp["kv_cache"].to(dev)
+                seqlens, table = inp["cache_seqlens"].to(dev), inp["block_table"].to(dev)
+                self.call = lambda: mx.mxfa_decode_splitkv_paged(q, cache, cq, seqlens, table, w.seqlen_q,
+                                                                 w.seqlen_k, head_dim_v=w.d_v, scale=scale,
+                                                                 workspace=ws, out=o, lse=lse)
+                self.kernel = "decode_mla_paged"
+            else:
+                kv, ck = inp["kv"].to(dev), inp["cu_seqlens_k"].to(dev)
+                self.call = lambda: mx.mxfa_decode_splitkv(q, kv, cq, ck, w.seqlen_q, w.seqlen_k,
+                                                           head_dim_v=w.d_v, scale=scale, workspace=ws, out=o,
+                                                           lse=lse)
+                self.kernel = "decode_mla"
+            del inp
         torch.cuda.synchronize()
 
     def time(self, steps, warmup):
@@ -336,7 +349,8 @@ def main():
     mx.load_library()  # fails loudly when the HIP library is not built
     names = args.workloads.split(",")
     if names == ["all"]:
-        names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16"]
+        names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16",
+                 "chunked_prefill_bf16", "paged_mla_decode_bf16"]
     if PRIMARY not in names:
         names.insert(0, PRIMARY)
 

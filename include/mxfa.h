@@ -130,6 +130,37 @@ mxfa_status mxfa_decode_splitkv(const void* q, const void* kv, void* o, float* l
                                 size_t workspace_bytes, mxfa_stream_t stream);
 
 /*
+ * Split-KV decode over a paged latent cache (the mxflashattn page's
+ * flash_attn_with_kvcache interface: k/v cache of fixed-size pages, per-batch
+ * cache_seqlens, block_table of page indices; the AstrAI v1.3.9 page's paged
+ * decode reads one page-table entry per key tile). Same computation and
+ * result as mxfa_decode_splitkv on the gathered keys.
+ *   kv_cache [num_pages, page_size, heads_kv, head_dim_qk] bf16
+ *   cache_seqlens int32 [batch]: keys of sequence b (bottom-right causal
+ *     alignment against its queries, as in mxfa_decode_splitkv)
+ *   block_table int32 [batch, max_pages], row-major, never NULL: key j of
+ *     sequence b is row j % page_size of page block_table[b * max_pages +
+ *     j / page_size]
+ * page_size: a positive multiple of 32 (one key tile never straddles a page).
+ * max_seqlen_k must bound cache_seqlens and be <= max_pages * page_size; it
+ * sizes the split plan (a longer sequence is cut to max_pages * page_size
+ * keys). Table entries of pages that hold keys must lie in [0, num_pages);
+ * a tile whose entry lies outside is read as zeros (no memory outside the
+ * cache is touched) and the affected rows' results are then unspecified.
+ * Entries past a sequence's last page are never read.
+ * Other arguments, the workspace and its size query as for
+ * mxfa_decode_splitkv.
+ */
+mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void* o, float* lse,
+                                      const int32_t* cu_seqlens_q, const int32_t* cache_seqlens,
+                                      const int32_t* block_table, int batch, int max_seqlen_q,
+                                      int max_seqlen_k, int total_q, int num_pages, int page_size,
+                                      int max_pages, int heads_q, int heads_kv, int head_dim_qk,
+                                      int head_dim_v, int causal, int window_left, int window_right,
+                                      float softcap, float scale, int num_splits, void* workspace,
+                                      size_t workspace_bytes, mxfa_stream_t stream);
+
+/*
  * Workspace bytes mxfa_decode_splitkv needs for these arguments (0 when
  * nothing is needed). With num_splits = 0 it queries the current device's
  * compute-unit count (a host-side HIP query, no device work); if that fails

@@ -176,3 +176,41 @@ def attention_dense(q, k, v, *, causal=False, window=(-1, -1), softcap=0.0, scal
                                  window=window, softcap=softcap, scale=scale, threads=threads,
                                  lib=lib)
     return o.reshape(b, sq, hq, -1), lse.reshape(b, sq, hq).transpose(0, 2, 1), dev
+
+
+def gather_paged(kv_cache, block_table, cache_seqlens):
+    """Packed keys of a paged cache.
+
+    The paged layout of the mxflashattn page's ``flash_attn_with_kvcache``
+    (block_table argument): the cache is ``[num_pages, page_size, H, d]`` and
+    key j of sequence b is row ``j mod page_size`` of page
+    ``block_table[b, j div page_size]``; sequence b holds
+    ``cache_seqlens[b]`` keys. Returns (kv ``[sum(cache_seqlens), H, d]``,
+    cu_k int32 ``[batch + 1]``), one key at a time in sequence order. Raises
+    ValueError for a page index outside the cache or a table row too short.
+    """
+    kv_cache = np.asarray(kv_cache)
+    table = np.asarray(block_table)
+    lens = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
+    num_pages, page_size = kv_cache.shape[0], kv_cache.shape[1]
+    if table.ndim != 2 or table.shape[0] != len(lens):
+        raise ValueError("block_table must be [batch, max_pages]")
+    rows = []
+    for b, n in enumerate(lens):
+        if n < 0:
+            raise ValueError("cache_seqlens must be >= 0")
+        for j in range(n):
+            logical = j // page_size
+            if logical >= table.shape[1]:
+                raise ValueError(f"sequence {b}: key {j} lies past its block_table row")
+            page = int(table[b, logical])
+            if not 0 <= page < num_pages:
+                raise ValueError(f"sequence {b}: page index {page} outside the cache")
+            rows.append(kv_cache[page, j % page_size])
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    if rows:
+        kv = np.stack(rows)
+    else:
+        kv = np.zeros((0,) + kv_cache.shape[2:], dtype=kv_cache.dtype)
+    return kv, cu

@@ -58,7 +58,8 @@ def _ctype_of(decl: str, named: bool = True):
 
 def test_header_declares_the_entry_points():
     names = set(_prototypes())
-    for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_decode_splitkv", "mxfa_decode_splitkv_workspace_bytes",
+    for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_decode_splitkv", "mxfa_decode_splitkv_paged",
+              "mxfa_decode_splitkv_workspace_bytes",
               "mxfa_decode_splitkv_num_splits", "mxfa_last_error", "mxfa_version"):
         assert n in names, n
 
@@ -141,6 +142,31 @@ def decode(lib, **kw):
 ])
 def test_decode_host_checks(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def paged(lib, **kw):
+    a = dict(q=A, kv=A, o=A, lse=A, cq=A, seqlens=A, table=A, batch=2, mq=4, mk=100, tq=8, pages=10, page=64,
+             max_pages=2, hq=16, hkv=1, dqk=576, dv=512, causal=0, wl=-1, wr=-1, softcap=0.0, scale=0.04,
+             splits=2, ws=A, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mxfa_decode_splitkv_paged(a["q"], a["kv"], a["o"], a["lse"], a["cq"], a["seqlens"], a["table"],
+                                         a["batch"], a["mq"], a["mk"], a["tq"], a["pages"], a["page"],
+                                         a["max_pages"], a["hq"], a["hkv"], a["dqk"], a["dv"], a["causal"],
+                                         a["wl"], a["wr"], a["softcap"], a["scale"], a["splits"], a["ws"],
+                                         a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(page=48), INVALID), (dict(page=0), INVALID), (dict(page=-32), INVALID), (dict(pages=-1), INVALID),
+    (dict(max_pages=-1), INVALID), (dict(max_pages=1), INVALID), (dict(mk=129), INVALID),
+    (dict(pages=1 << 26, page=64), INVALID), (dict(table=None), INVALID), (dict(seqlens=None), INVALID),
+    (dict(table=A + 2), INVALID), (dict(kv=None), INVALID), (dict(dqk=128, dv=128), UNSUPPORTED),
+    (dict(ws=None), WORKSPACE), (dict(splits=65), INVALID), (dict(batch=0), OK),
+])
+def test_paged_decode_host_checks(lib, kw, status):
+    assert paged(lib, **kw) == status
+    if status != OK:
+        assert lib.mxfa_last_error().decode()
 
 
 @pytest.mark.parametrize("batch,mq,mk,hq,hkv,splits", [(128, 4, 8192, 16, 1, 2), (3, 9, 100, 16, 2, 5),

@@ -245,6 +245,77 @@ def test_decode_independent_of_split_count():
     assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
 
 
+# ------------------------------------------------------- paged-cache decode
+
+# (lens_q, lens_k, hq, hkv, causal, window, softcap, splits, page_size)
+PAGED_CASES = [
+    ([1, 4, 2], [1, 70, 300], 16, 1, False, (-1, -1), 0.0, 0, 32),
+    ([4, 4], [1000, 129], 16, 1, True, (-1, -1), 0.0, 3, 64),
+    ([4, 1, 3], [500, 0, 65], 16, 2, True, (100, 0), 30.0, 4, 128),
+    ([9, 1], [700, 256], 16, 1, False, (-1, -1), 0.0, 5, 256),
+]
+
+
+def _paged_problem(seed, lq, lk, hq, hkv, page_size):
+    p = workloads.make_problem(seed, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    gen = torch.Generator("cpu").manual_seed(seed + 1)
+    # Rows no key fills hold NaN and table entries past each sequence's last
+    # page point far outside the cache: a read of either would show.
+    pg = workloads.paginate(p["kv"], lk, page_size, gen, spare_pages=3, fill=float("nan"), table_pad=2,
+                            pad_value=1 << 30)
+    return p, pg
+
+
+def _run_paged(p, pg, causal, window, cap, splits, scale):
+    d = dev()
+    o, lse = mx.mxfa_decode_splitkv_paged(p["q"].to(d), pg["kv_cache"].to(d), p["cu_seqlens_q"].to(d),
+                                          pg["cache_seqlens"].to(d), pg["block_table"].to(d), max(p["lens_q"]),
+                                          max(p["lens_k"]), head_dim_v=512, causal=causal, window=window,
+                                          softcap=cap, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", PAGED_CASES, ids=[f"paged{i}" for i in range(len(PAGED_CASES))])
+def test_paged_decode_matches_oracle(case):
+    lq, lk, hq, hkv, causal, window, cap, splits, page = case
+    seed = 3300 + PAGED_CASES.index(case)
+    print(f"[paged] {case} seed={seed}", flush=True)
+    p, pg = _paged_problem(seed, lq, lk, hq, hkv, page)
+    scale = 1.0 / math.sqrt(576)
+    o_g, lse_g = _run_paged(p, pg, causal, window, cap, splits, scale)
+    import oracle
+
+    kv, ck = oracle.gather_paged(to_np(pg["kv_cache"]), pg["block_table"].numpy(), pg["cache_seqlens"].numpy())
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kv, kv[:, :, :512], p["cu_seqlens_q"].numpy(), ck,
+                                              causal=causal, window=window, softcap=cap, scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            str(case))
+    # Same split plan, same arithmetic: the paged call equals the contiguous one bit for bit.
+    o_c, lse_c = _run_decode(p, hq, causal, window, cap, splits, scale)
+    assert np.array_equal(o_g, o_c) and np.array_equal(lse_g, lse_c)
+
+
+def test_paged_decode_bad_page_index_touches_only_its_sequence():
+    # A page index outside the cache in a page that holds keys: that tile
+    # reads as zeros (no memory outside the cache is read); the other
+    # sequences stay exact.
+    p, pg = _paged_problem(3390, [4, 4], [300, 200], 16, 1, 64)
+    pg["block_table"][0, 1] = pg["kv_cache"].shape[0] + 5
+    print("[paged] bad page index", flush=True)
+    scale = 1.0 / math.sqrt(576)
+    o_g, lse_g = _run_paged(p, pg, False, (-1, -1), 0.0, 2, scale)
+    assert np.all(np.isfinite(o_g)) and np.all(np.isfinite(lse_g))
+    import oracle
+
+    kv = to_np(p["kv"])
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kv, kv[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), scale=scale)
+    compare(o_g[4:].reshape(-1, 512), lse_g[:, 4:].T.reshape(-1), o_ref[4:].reshape(-1, 512),
+            lse_ref[4:].reshape(-1), "bf16", "sequence 1")
+
+
 # --------------------------------------------------- headline workloads, full size
 
 def _full_dense_or_varlen(name, n_rows):
@@ -311,6 +382,11 @@ def test_full_window_softcap_bf16():
     _full_dense_or_varlen("window_softcap_bf16", 384)
 
 
+def test_full_chunked_prefill_bf16():
+    # Sq < Sk: the chunk's rows see the whole cached prefix plus their causal part.
+    _full_dense_or_varlen("chunked_prefill_bf16", 384)
+
+
 def test_full_mla_decode_bf16():
     w = workloads.get("mla_decode_bf16")
     print("[full] mla_decode_bf16: generating inputs", flush=True)
@@ -329,3 +405,44 @@ def test_full_mla_decode_bf16():
     o_c = o.float().cpu().numpy()
     lse_c = lse.T.cpu().numpy()
     compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "mla_decode_bf16")
+
+
+def test_full_paged_mla_decode_bf16():
+    w = workloads.get("paged_mla_decode_bf16")
+    print("[full] paged_mla_decode_bf16: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    d = dev()
+    q = inp["q"].to(d)
+    cq = inp["cu_seqlens_q"].to(d)
+    cache = inp["kv_cache"].to(d)
+    o, lse = mx.mxfa_decode_splitkv_paged(q, cache, cq, inp["cache_seqlens"].to(d), inp["block_table"].to(d),
+                                          w.seqlen_q, w.seqlen_k, head_dim_v=w.d_v, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    del cache
+    rows = sample_rows(inp["lens_q"], w.heads_q, 256, seed=w.seed)
+    import oracle
+
+    # The oracle reads the keys through the block table only for the sampled
+    # rows' sequences: gather those, then run the rows against them.
+    seqs = sorted({int(t) // w.seqlen_q for t in rows[:, 0]})
+    kv_parts = []
+    for b in seqs:
+        kv_b, _ = oracle.gather_paged(to_np(inp["kv_cache"]), inp["block_table"][b:b + 1].numpy(),
+                                      inp["cache_seqlens"][b:b + 1].numpy())
+        kv_parts.append(kv_b)
+    kvn = np.concatenate(kv_parts)
+    q_n = to_np(inp["q"]).reshape(w.batch, w.seqlen_q, w.heads_q, w.d_qk)[seqs].reshape(-1, w.heads_q, w.d_qk)
+    cu = np.arange(len(seqs) + 1, dtype=np.int32)
+    slot = {b: i for i, b in enumerate(seqs)}
+    local = np.stack([[slot[int(t) // w.seqlen_q] * w.seqlen_q + int(t) % w.seqlen_q, h] for t, h in rows])
+    o_ref, lse_ref, _ = oracle.attention_rows(q_n, kvn, kvn[:, :, :w.d_v], cu * w.seqlen_q, cu * w.seqlen_k,
+                                              scale=w.softmax_scale, rows=local)
+    o_c = o.float().cpu().numpy()
+    lse_c = lse.T.cpu().numpy()
+    compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16",
+            "paged_mla_decode_bf16")
+    # Bit for bit the contiguous call on the packed keys (same split plan).
+    o2, lse2 = mx.mxfa_decode_splitkv(q, inp["kv"].to(d), cq, inp["cu_seqlens_k"].to(d), w.seqlen_q, w.seqlen_k,
+                                      head_dim_v=w.d_v, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)

@@ -323,6 +323,43 @@ def test_row_selection_matches_full():
         assert np.array_equal(os_[n], o[t, h]) and ls[n] == lse[t, h]
 
 
+# -------------------------------------------------------------- paged cache
+
+def test_gather_paged_worked_example():
+    # Three pages of two rows; row r of page g holds the value 10 g + r. Key j
+    # of sequence b is row j mod 2 of page table[b][j div 2]: sequence 0
+    # (3 keys, pages 2 then 0) reads 20, 21, 0; sequence 1 (1 key, page 1)
+    # reads 10, and its second table entry (7, outside the cache) lies past
+    # its last page, so it is never read.
+    cache = np.array([[[[10.0 * g + r]] for r in range(2)] for g in range(3)], dtype=np.float32)
+    table = np.array([[2, 0], [1, 7]], dtype=np.int32)
+    kv, cu = oracle.gather_paged(cache, table, [3, 1])
+    assert cu.tolist() == [0, 3, 4]
+    assert kv.reshape(-1).tolist() == [20.0, 21.0, 0.0, 10.0]
+
+
+def test_gather_paged_rejects_bad_pages():
+    cache = np.zeros((2, 4, 1, 8), dtype=np.float32)
+    with pytest.raises(ValueError):
+        oracle.gather_paged(cache, np.array([[0, 2]], dtype=np.int32), [5])  # page 2 of 2
+    with pytest.raises(ValueError):
+        oracle.gather_paged(cache, np.array([[1]], dtype=np.int32), [5])  # needs 2 table entries
+
+
+@pytest.mark.parametrize("page_size,lens", [(32, [1, 70, 300]), (64, [64, 0, 128]), (128, [500, 65])])
+def test_gather_paged_inverts_paginate(page_size, lens):
+    # The input generator scatters packed keys into shuffled pages; gathering
+    # them back through the table must give the packed keys exactly.
+    gen = torch.Generator("cpu").manual_seed(77)
+    kv = torch.randn(sum(lens), 2, 16, generator=gen).to(torch.bfloat16)
+    pg = workloads.paginate(kv, lens, page_size, gen, spare_pages=3, fill=float("nan"), table_pad=2,
+                            pad_value=1 << 30)
+    back, cu = oracle.gather_paged(workloads.to_numpy_bits(pg["kv_cache"]), pg["block_table"].numpy(),
+                                   pg["cache_seqlens"].numpy())
+    assert np.array_equal(back, workloads.to_numpy_bits(kv))
+    assert cu.tolist() == [0] + np.cumsum(lens).tolist()
+
+
 # ----------------------------------------------------------- planted mistakes
 
 MUTANTS = {

@@ -22,6 +22,7 @@ __all__ = [
     "mxfa_fwd",
     "mxfa_fwd_varlen",
     "mxfa_decode_splitkv",
+    "mxfa_decode_splitkv_paged",
     "mxfa_decode_splitkv_workspace_bytes",
     "mxfa_decode_splitkv_num_splits",
     "mxfa_version",
@@ -42,6 +43,7 @@ _SIGNATURES = {
     "mxfa_fwd": (_c_int, [_vp] * 5 + [_c_int] * 10 + [_c_float, _c_float, _vp]),
     "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp]),
     "mxfa_decode_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
+    "mxfa_decode_splitkv_paged": (_c_int, [_vp] * 7 + [_c_int] * 14 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_workspace_bytes": (_sz, [_c_int] * 7),
     "mxfa_decode_splitkv_num_splits": (_c_int, [_c_int] * 6),
     "mxfa_last_error": (ctypes.c_char_p, []),
@@ -234,5 +236,54 @@ def mxfa_decode_splitkv(q, kv, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seq
                                      int(window[1]), float(softcap), _scale(scale, dqk), int(num_splits),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(dev))
+    _check(st)
+    return out, lse
+
+
+def mxfa_decode_splitkv_paged(q, kv_cache, cu_seqlens_q, cache_seqlens, block_table, max_seqlen_q, max_seqlen_k, *,
+                              head_dim_v=512, causal=False, window=(-1, -1), softcap=0.0, scale=None,
+                              num_splits=0, workspace=None, out=None, lse=None, return_lse=True):
+    """Latent-KV split decode over a paged cache.
+
+    q [Tq,Hq,576] bf16; kv_cache [num_pages, page_size, Hkv, 576] bf16;
+    cache_seqlens int32 [B]; block_table int32 [B, max_pages]: sequence b's key
+    j is row j % page_size of page block_table[b, j // page_size]. V is
+    kv[..., :head_dim_v]. Returns (o [Tq,Hq,head_dim_v] bf16, lse [Hq,Tq] fp32).
+    """
+    lib = load_library()
+    _need(q.dim() == 3 and kv_cache.dim() == 4, "q must be [T, H, d] and kv_cache [pages, page_size, H, d]")
+    tq, hq, dqk = q.shape
+    num_pages, page_size, hkv = kv_cache.shape[0], kv_cache.shape[1], kv_cache.shape[2]
+    _need(kv_cache.shape[3] == dqk, "q and kv_cache head dims differ")
+    _need(kv_cache.dtype == q.dtype, "q and kv_cache must share a dtype")
+    _need(q.dtype == torch.bfloat16, "decode supports bf16")
+    _need(cu_seqlens_q.dtype == torch.int32 and cache_seqlens.dtype == torch.int32 and
+          block_table.dtype == torch.int32, "cu_seqlens_q, cache_seqlens and block_table must be int32")
+    _need(cu_seqlens_q.dim() == 1 and cache_seqlens.dim() == 1 and block_table.dim() == 2,
+          "cu_seqlens_q [B+1], cache_seqlens [B], block_table [B, max_pages]")
+    batch = cu_seqlens_q.shape[0] - 1
+    _need(cache_seqlens.shape[0] == batch and block_table.shape[0] == batch, "batch sizes differ")
+    if out is None:
+        out = torch.empty((tq, hq, head_dim_v), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need(out.shape == (tq, hq, head_dim_v) and out.dtype == q.dtype, "out must be [Tq,Hq,head_dim_v]")
+    _need(lse is None or (lse.shape == (hq, tq) and lse.dtype == torch.float32), "lse must be [Hq,Tq] fp32")
+    dev = _tensors_ok(q, kv_cache, out, lse, cu_seqlens_q, cache_seqlens, block_table, workspace)
+    max_pages = block_table.shape[1]
+    if block_table.numel() == 0:  # the C call wants a non-null table even when it holds no pages
+        block_table = torch.zeros(1, dtype=torch.int32, device=q.device)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            nbytes = mxfa_decode_splitkv_workspace_bytes(batch, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
+                                                         head_dim_v, num_splits)
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        st = lib.mxfa_decode_splitkv_paged(_ptr(q), _ptr(kv_cache), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                           _ptr(cache_seqlens), _ptr(block_table), batch, int(max_seqlen_q),
+                                           int(max_seqlen_k), tq, num_pages, page_size, max_pages,
+                                           hq, hkv, dqk, int(head_dim_v), int(bool(causal)), int(window[0]),
+                                           int(window[1]), float(softcap), _scale(scale, dqk), int(num_splits),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(dev))
     _check(st)
     return out, lse

@@ -58,7 +58,7 @@ static_assert(LOADS * 16 * NTHREADS == TILEB, "tile must split into whole loads"
 // (transposing V reads).
 MXFA_DEV int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
-template <bool kCap>
+template <bool kCap, bool kPaged>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_kernel(const DecodeParams p) {
     // Five LDS objects: a reader of one stage then never waits for the loads
@@ -80,8 +80,10 @@ void decode_split_kernel(const DecodeParams p) {
 
     const int q_start = p.cu_q[b];
     const int sq = p.cu_q[b + 1] - q_start;
-    const int k_start = p.cu_k[b];
-    const int sk = p.cu_k[b + 1] - k_start;
+    // Paged cache: sequence b's keys sit in pages block_table[b][*] of
+    // page_size rows each; its length is capped at what its table row holds.
+    const int k_start = kPaged ? 0 : p.cu_k[b];
+    const int sk = kPaged ? max(0, min(p.seqlens_k[b], p.max_pages * p.page_size)) : p.cu_k[b + 1] - k_start;
     const int row0 = mg * ROWS;
     const int nrows = sq * G;
     if (row0 >= nrows) return;
@@ -176,19 +178,45 @@ void decode_split_kernel(const DecodeParams p) {
         return (uint32_t)(row * (int)(kv_tok_stride * 2) + c * 16);
     };
     const uint16_t* KVseg = static_cast<const uint16_t*>(p.kv) + (long long)k_start * kv_tok_stride + (long long)g * DQK;
-    // Tiles past the key range are issued too, as loads of zero bytes (a
-    // buffer resource of size 0 returns zeros without touching memory), so
-    // every step has the same number of loads in flight behind it. A tile's
-    // loads may be issued in parts (loads [n0, n1)).
-    auto issue_part = [&](int kt, char* stage, int n0, int n1) __attribute__((always_inline)) {
+    // Paged cache: physical page of the tile at key kt (a tile never
+    // straddles a page, pages holding a multiple of BN keys); 0 for tiles
+    // past the keys, which are never read. Read one step before its use.
+    // The table is read through the constant address space: it is not
+    // written while the kernel runs, and so the read becomes a scalar load,
+    // kept out of the vector-memory count that the stage waits rely on.
+    using ConstI32 = const __attribute__((address_space(4))) int32_t;
+    auto page_of = [&](int kt) __attribute__((always_inline)) -> int {
+        if (!kPaged || kt >= sk) return 0;
+        const ConstI32* tab = (const ConstI32*)p.block_table;
+        return tab[(long long)b * p.max_pages + kt / p.page_size];
+    };
+    // Buffer resource over the tile at key kt: its rows up to the last key
+    // (rows past it read as zeros). Tiles past the key range, and tiles
+    // whose page number lies outside the cache, get a resource of zero
+    // bytes: their loads return zeros without touching memory.
+    auto tile_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
         long long bytes = (long long)(sk - kt - 1) * kv_tok_stride * 2 + DQK * 2;
+        const uint16_t* base = KVseg + (long long)kt * kv_tok_stride;
+        if (kPaged) {
+            if ((unsigned)phys >= (unsigned)p.num_pages) bytes = 0;
+            else
+                base = static_cast<const uint16_t*>(p.kv) +
+                       ((long long)phys * p.page_size + kt % p.page_size) * kv_tok_stride + (long long)g * DQK;
+        }
         if (kt >= sk) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(KVseg + (long long)kt * kv_tok_stride, (uint32_t)bytes);
+        return make_rsrc(bytes ? base : KVseg, (uint32_t)bytes);
+    };
+    // Tiles past the key range are issued too, as loads of zero bytes, so
+    // every step has the same number of loads in flight behind it. A tile's
+    // loads may be issued in parts (loads [n0, n1)).
+    auto issue_part = [&](const __amdgpu_buffer_rsrc_t& r, char* stage, int n0, int n1) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = n0; n < n1; ++n) buffer_load_lds16(r, stage + (n * NTHREADS + w * 64) * 16, goff(n));
     };
-    auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) { issue_part(kt, stage, 0, LOADS); };
+    auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) {
+        issue_part(tile_rsrc(kt, page_of(kt)), stage, 0, LOADS);
+    };
 
     // O^T accumulators: channel block cb (channels 256*ch + 32*cb + ...), column lr.
     f32x16_t acc[CBLK];
@@ -343,6 +371,7 @@ void decode_split_kernel(const DecodeParams p) {
         issue_tile(kt0, sT0);
         issue_tile(kt0 + BN, sT1);
         issue_tile(kt0 + 2 * BN, sT2);
+        int phys_fill = page_of(kt0 + 3 * BN);  // page of the tile the next step issues
         asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's loads of tile 0
         lds_barrier();
         if (block_active) {
@@ -368,17 +397,19 @@ void decode_split_kernel(const DecodeParams p) {
             const int kt_fill = kt0 + (j + 3) * BN;  // tile j+3 -> the stage of tile j-1
             uint32_t pk[8];
             float alpha = 1.0f;
-            issue_part(kt_fill, prv, 0, 3);
+            const __amdgpu_buffer_rsrc_t rfill = tile_rsrc(kt_fill, phys_fill);
+            phys_fill = page_of(kt_fill + BN);
+            issue_part(rfill, prv, 0, 3);
             if (block_active) {
                 // On the last step this reads a finished (zero-filled) tile;
                 // the result is not used.
                 s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha,
-                                    [&]() __attribute__((always_inline)) { issue_part(kt_fill, prv, 3, 6); });
+                                    [&]() __attribute__((always_inline)) { issue_part(rfill, prv, 3, 6); });
             } else {
-                issue_part(kt_fill, prv, 3, 6);
+                issue_part(rfill, prv, 3, 6);
             }
             lds_barrier();
-            issue_part(kt_fill, prv, 6, LOADS);
+            issue_part(rfill, prv, 6, LOADS);
             if (block_active) {
                 if (j + 1 < ntiles) publish();
                 if (wave_any(alpha != 1.0f)) {
@@ -494,10 +525,15 @@ hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream) {
     if (units <= 0) return hipSuccess;
     const long long grid_split = units * p.splits;
     if (grid_split > 0x7fffffffLL || units * (ROWS / CROWS) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((decode_split_kernel<true>), dim3((unsigned)grid_split), dim3(NTHREADS), 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_split_kernel<false>), dim3((unsigned)grid_split), dim3(NTHREADS), 0, stream, p);
+    const dim3 grid((unsigned)grid_split);
+    const bool cap = p.softcap > 0.0f;
+    if (p.block_table) {
+        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(NTHREADS), 0, stream, p);
+    } else {
+        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(NTHREADS), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(units * (ROWS / CROWS))), dim3(NTHREADS), 0, stream, p);

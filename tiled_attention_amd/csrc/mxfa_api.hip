@@ -126,6 +126,79 @@ size_t decode_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, i
     return (size_t)parts * (size_t)mxfa::kDecodeRows * ((size_t)head_dim_v + 2) * sizeof(float);
 }
 
+// Checks and launch shared by the contiguous (cu_k) and paged (pg) decode
+// entry points; exactly one of cu_k and pg is non-null. total_k: key rows in kv.
+mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, const mxfa::PagedKV* pg, int batch, int max_seqlen_q,
+                          int max_seqlen_k, int total_q, int total_k, int heads_q, int heads_kv, int head_dim_qk,
+                          int head_dim_v, int causal, int window_left, int window_right, float softcap, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, mxfa_stream_t stream) {
+    if (head_dim_qk != 576 || head_dim_v != 512)
+        return fail(MXFA_ERR_UNSUPPORTED, "decode head dims (%d, %d): supported (576, 512)", head_dim_qk, head_dim_v);
+    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+        return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
+    if (max_seqlen_q > total_q) return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(MXFA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", kMaxSplits);
+    mxfa_status st = check_common(heads_q, heads_kv, window_left, window_right, softcap, scale);
+    if (st != MXFA_OK) return st;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return MXFA_OK;
+    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) != MXFA_OK) return st;
+    if (pg) {
+        if ((st = check_tensor(pg->seqlens, "cache_seqlens", 4)) != MXFA_OK) return st;
+        if ((st = check_tensor(pg->block_table, "block_table", 4)) != MXFA_OK) return st;
+    } else if ((st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)) != MXFA_OK) {
+        return st;
+    }
+    if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
+    if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
+    if (total_k > 0 && (st = check_tensor(kv, "kv", 16)) != MXFA_OK) return st;
+    if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+
+    int err = 0;
+    const int splits = plan_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits, &err);
+    if (err) return hip_fail((hipError_t)err, "device query for the split count");
+    const size_t need = decode_ws_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim_v, splits);
+    if (!workspace || workspace_bytes < need)
+        return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+
+    mxfa::DecodeParams p = {};
+    p.q = q;
+    p.kv = kv;
+    p.o = o;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.batch = batch;
+    p.max_seqlen_q = max_seqlen_q;
+    p.max_seqlen_k = max_seqlen_k;
+    p.total_q = total_q;
+    p.heads_q = heads_q;
+    p.heads_kv = heads_kv;
+    p.group = heads_q / heads_kv;
+    p.m_groups = (int)(((long long)max_seqlen_q * p.group + mxfa::kDecodeRows - 1) / mxfa::kDecodeRows);
+    p.splits = splits;
+    const long long parts = (long long)batch * heads_kv * p.m_groups * splits;
+    p.part_acc = static_cast<float*>(workspace);
+    p.part_ml = p.part_acc + parts * mxfa::kDecodeRows * head_dim_v;
+    p.causal = causal ? 1 : 0;
+    p.window_left = window_left;
+    p.window_right = window_right;
+    p.softcap = softcap;
+    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    if (pg) {
+        p.block_table = pg->block_table;
+        p.seqlens_k = pg->seqlens;
+        p.page_size = pg->page_size;
+        p.max_pages = pg->max_pages;
+        p.num_pages = pg->num_pages;
+    }
+    hipError_t e = mxfa::launch_decode_mla(p, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return MXFA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,59 +331,35 @@ mxfa_status mxfa_decode_splitkv(const void* q, const void* kv, void* o, float* l
                                 float scale, int num_splits, void* workspace, size_t workspace_bytes,
                                 mxfa_stream_t stream) {
     g_err[0] = 0;
-    if (head_dim_qk != 576 || head_dim_v != 512)
-        return fail(MXFA_ERR_UNSUPPORTED, "decode head dims (%d, %d): supported (576, 512)", head_dim_qk, head_dim_v);
-    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
-        return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
-    if (max_seqlen_q > total_q || max_seqlen_k > total_k)
-        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
-    if (num_splits < 0 || num_splits > kMaxSplits)
-        return fail(MXFA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", kMaxSplits);
-    mxfa_status st = check_common(heads_q, heads_kv, window_left, window_right, softcap, scale);
-    if (st != MXFA_OK) return st;
-    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return MXFA_OK;
-    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) != MXFA_OK) return st;
-    if ((st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)) != MXFA_OK) return st;
-    if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
-    if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
-    if (total_k > 0 && (st = check_tensor(kv, "kv", 16)) != MXFA_OK) return st;
-    if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    if (total_k < 0) return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
+    if (max_seqlen_k > total_k) return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
+    return decode_common(q, kv, o, lse, cu_seqlens_q, cu_seqlens_k, nullptr, batch, max_seqlen_q, max_seqlen_k,
+                         total_q, total_k, heads_q, heads_kv, head_dim_qk, head_dim_v, causal, window_left,
+                         window_right, softcap, scale, num_splits, workspace, workspace_bytes, stream);
+}
 
-    int err = 0;
-    const int splits = plan_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits, &err);
-    if (err) return hip_fail((hipError_t)err, "device query for the split count");
-    const size_t need = decode_ws_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim_v, splits);
-    if (!workspace || workspace_bytes < need)
-        return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : 0);
-    if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-
-    mxfa::DecodeParams p = {};
-    p.q = q;
-    p.kv = kv;
-    p.o = o;
-    p.lse = lse;
-    p.cu_q = cu_seqlens_q;
-    p.cu_k = cu_seqlens_k;
-    p.batch = batch;
-    p.max_seqlen_q = max_seqlen_q;
-    p.max_seqlen_k = max_seqlen_k;
-    p.total_q = total_q;
-    p.heads_q = heads_q;
-    p.heads_kv = heads_kv;
-    p.group = heads_q / heads_kv;
-    p.m_groups = (int)(((long long)max_seqlen_q * p.group + mxfa::kDecodeRows - 1) / mxfa::kDecodeRows);
-    p.splits = splits;
-    const long long parts = (long long)batch * heads_kv * p.m_groups * splits;
-    p.part_acc = static_cast<float*>(workspace);
-    p.part_ml = p.part_acc + parts * mxfa::kDecodeRows * head_dim_v;
-    p.causal = causal ? 1 : 0;
-    p.window_left = window_left;
-    p.window_right = window_right;
-    p.softcap = softcap;
-    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
-    hipError_t e = mxfa::launch_decode_mla(p, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
-    return MXFA_OK;
+mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void* o, float* lse,
+                                      const int32_t* cu_seqlens_q, const int32_t* cache_seqlens,
+                                      const int32_t* block_table, int batch, int max_seqlen_q, int max_seqlen_k,
+                                      int total_q, int num_pages, int page_size, int max_pages, int heads_q,
+                                      int heads_kv, int head_dim_qk, int head_dim_v, int causal, int window_left,
+                                      int window_right, float softcap, float scale, int num_splits,
+                                      void* workspace, size_t workspace_bytes, mxfa_stream_t stream) {
+    g_err[0] = 0;
+    if (num_pages < 0 || max_pages < 0)
+        return fail(MXFA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 0");
+    if (page_size <= 0 || page_size % mxfa::kDecodeTile)
+        return fail(MXFA_ERR_INVALID_ARG, "page_size %d: must be a positive multiple of %d", page_size,
+                    mxfa::kDecodeTile);
+    if ((long long)max_seqlen_k > (long long)max_pages * page_size)
+        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen_k %d exceeds the block table's %lld keys", max_seqlen_k,
+                    (long long)max_pages * page_size);
+    if ((long long)num_pages * page_size > 0x7fffffffLL)
+        return fail(MXFA_ERR_INVALID_ARG, "the cache holds more than 2^31 - 1 rows");
+    mxfa::PagedKV pg = {block_table, cache_seqlens, page_size, max_pages, num_pages};
+    return decode_common(q, kv_cache, o, lse, cu_seqlens_q, nullptr, &pg, batch, max_seqlen_q, max_seqlen_k,
+                         total_q, num_pages * page_size, heads_q, heads_kv, head_dim_qk, head_dim_v, causal,
+                         window_left, window_right, softcap, scale, num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -63,6 +63,21 @@ struct DecodeParams {
     float x_mul;
     float cap_mul;
     float cap_out;
+    // Paged latent cache (null block_table: contiguous kv with cu_k).
+    const int32_t* block_table;  // [batch, max_pages] physical page of each logical page
+    const int32_t* seqlens_k;    // [batch] keys of each sequence
+    int page_size;               // keys per page, a multiple of kDecodeTile
+    int max_pages;               // row length of block_table
+    int num_pages;               // pages in the cache (kv holds num_pages * page_size rows)
+};
+
+// Page-table description of a paged latent cache, as the host receives it.
+struct PagedKV {
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    int page_size;
+    int max_pages;
+    int num_pages;
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);

@@ -8,7 +8,8 @@ Recipe (the same for every workload):
 
 * one ``torch.Generator('cpu')`` seeded with the workload's seed;
 * draw order: packed-batch lengths (when the workload has them), then q, then
-  k, then v -- or q then the shared latent kv for the latent-KV decode;
+  k, then v -- or q then the shared latent kv for the latent-KV decode, then
+  (paged cache only) one permutation of the physical page indices;
 * values are float32 ``randn`` (N(0, 1)); bf16 workloads cast them with
   round-to-nearest-even (torch's ``.to(torch.bfloat16)``). The stored,
   already-rounded tensors are the inputs to both sides of every comparison.
@@ -16,7 +17,8 @@ Recipe (the same for every workload):
 Layouts: dense ``[B, S, H, d]``; packed (varlen) ``[total, H, d]`` with int32
 ``cu_seqlens`` of length ``batch + 1`` starting at 0; latent-KV decode keeps a
 single ``kv`` buffer ``[total_k, H_kv, d_qk]`` whose first ``d_v`` channels are
-V.
+V; its paged form (``paginate``) is a cache ``[num_pages, page_size, H_kv,
+d_qk]`` with an int32 ``block_table [B, max_pages]`` and ``cache_seqlens [B]``.
 """
 from __future__ import annotations
 
@@ -32,6 +34,7 @@ __all__ = [
     "get",
     "make_inputs",
     "make_problem",
+    "paginate",
     "varlen_lengths",
     "to_numpy_bits",
 ]
@@ -58,6 +61,7 @@ class Workload:
     window: tuple = (-1, -1)
     softcap: float = 0.0
     scale: Optional[float] = None  # None -> d_qk ** -0.5
+    page_size: int = 0  # decode: > 0 stores the latent kv in a paged cache of this many rows per page
     note: str = field(default="", compare=False)
 
     @property
@@ -65,8 +69,8 @@ class Workload:
         return float(self.scale) if self.scale is not None else 1.0 / math.sqrt(self.d_qk)
 
 
-# The five workloads of the method's headline configurations. Seeds are the
-# configuration index.
+# The five workloads of the method's headline configurations (seeds are the
+# configuration index), then further workloads.
 WORKLOADS = {
     "single_head_f32": Workload(
         name="single_head_f32", seed=0, kind="dense", dtype="f32", batch=1, heads_q=1,
@@ -90,6 +94,20 @@ WORKLOADS = {
         heads_kv=8, d_qk=128, d_v=128, seqlen_q=32768, seqlen_k=32768, causal=True,
         window=(4096, 0), softcap=50.0,
         note="B=1 Hq=32 Hkv=8 S=32768 d=128 bf16, causal, window (4096,0), softcap 50"),
+    # Beyond the headline set: a prefill chunk of 2048 new tokens attending to
+    # a 16384-token sequence whose first 14336 tokens are already cached
+    # (Sq < Sk, bottom-right causal alignment).
+    "chunked_prefill_bf16": Workload(
+        name="chunked_prefill_bf16", seed=5, kind="dense", dtype="bf16", batch=2, heads_q=32,
+        heads_kv=8, d_qk=128, d_v=128, seqlen_q=2048, seqlen_k=16384, causal=True,
+        note="B=2 Hq=32 Hkv=8 Sq=2048 Sk=16384 d=128 bf16, causal (chunk after a 14336-token cache)"),
+    # The latent-KV decode above with its cache in 64-row pages, placed at
+    # shuffled physical page indices.
+    "paged_mla_decode_bf16": Workload(
+        name="paged_mla_decode_bf16", seed=6, kind="decode", dtype="bf16", batch=128, heads_q=16,
+        heads_kv=1, d_qk=576, d_v=512, seqlen_q=4, seqlen_k=8192, causal=False,
+        scale=1.0 / math.sqrt(576), page_size=64,
+        note="mla_decode_bf16's shapes, kv in a paged cache of 64-row pages, shuffled page order"),
 }
 
 
@@ -161,6 +179,39 @@ def make_problem(seed: int, *, dtype: str, heads_q: int, heads_kv: int, d_qk: in
     return out
 
 
+def paginate(kv: torch.Tensor, lens_k, page_size: int, gen: torch.Generator, *, spare_pages: int = 0,
+             fill: float = 0.0, table_pad: int = 0, pad_value: int = -1) -> dict:
+    """Scatter packed keys ``kv [sum(lens_k), H, d]`` into a paged cache.
+
+    Sequence b takes ceil(len_b / page_size) pages; the physical page of each
+    logical page comes from one ``torch.randperm`` (drawn from ``gen``) over
+    all pages, ``spare_pages`` extra pages included. Rows no key fills (the
+    tail of each sequence's last page, the spare pages) hold ``fill``; each
+    table row is padded with ``pad_value`` to the longest sequence's page
+    count plus ``table_pad``. Returns ``kv_cache [num_pages, page_size, H, d]``,
+    ``block_table`` int32 ``[B, max_pages]`` and ``cache_seqlens`` int32 ``[B]``.
+    """
+    lens = [int(x) for x in lens_k]
+    pages_of = [(n + page_size - 1) // page_size for n in lens]
+    used = sum(pages_of)
+    num_pages = used + spare_pages
+    perm = torch.randperm(num_pages, generator=gen)
+    cache = torch.full((num_pages, page_size) + tuple(kv.shape[1:]), fill, dtype=kv.dtype)
+    max_pages = (max(pages_of) if pages_of else 0) + table_pad
+    table = torch.full((len(lens), max_pages), pad_value, dtype=torch.int32)
+    nxt = 0
+    start = 0
+    for b, n in enumerate(lens):
+        for lp in range(pages_of[b]):
+            phys = int(perm[nxt])
+            nxt += 1
+            table[b, lp] = phys
+            rows = min(page_size, n - lp * page_size)
+            cache[phys, :rows] = kv[start + lp * page_size:start + lp * page_size + rows]
+        start += n
+    return {"kv_cache": cache, "block_table": table, "cache_seqlens": torch.tensor(lens, dtype=torch.int32)}
+
+
 def make_inputs(w: Workload) -> dict:
     """The inputs of workload ``w`` (see the module docstring for the recipe)."""
     gen = torch.Generator("cpu").manual_seed(int(w.seed))
@@ -175,6 +226,8 @@ def make_inputs(w: Workload) -> dict:
     out["q"] = _draw(gen, (tq, w.heads_q, w.d_qk), w.dtype)
     if w.kind == "decode":
         out["kv"] = _draw(gen, (tk, w.heads_kv, w.d_qk), w.dtype)
+        if w.page_size:
+            out.update(paginate(out["kv"], lens_k, w.page_size, gen))
     else:
         out["k"] = _draw(gen, (tk, w.heads_kv, w.d_qk), w.dtype)
         out["v"] = _draw(gen, (tk, w.heads_kv, w.d_v), w.dtype)
