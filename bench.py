@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "fwd_f32": "tiled_attention_amd/csrc/fwd_f32.hip",
     "decode_mla": "tiled_attention_amd/csrc/decode_mla.hip",
     "decode_mla_paged": "tiled_attention_amd/csrc/decode_mla.hip",
+    "decode_gqa": "tiled_attention_amd/csrc/decode_gqa.hip",
 }
 
 
@@ -102,6 +103,7 @@ PMC_KERNELS = {
     "fwd_bf16": ("fwd_bf16_kernel<128, 0>",),
     "decode_mla": ("decode_split_kernel<false, false>", "decode_combine_kernel"),
     "decode_mla_paged": ("decode_split_kernel<false, true>", "decode_combine_kernel"),
+    "decode_gqa": ("decode_gqa_split_kernel<128, false>", "decode_gqa_combine_kernel<128>"),
 }
 COPY_KERNEL_MARKERS = ("copyBuffer", "copy_kernel", "CopyKernel")
 
@@ -191,6 +193,20 @@ class Runner:
             self.call = lambda: mx.mxfa_fwd(q, k, v, causal=w.causal, window=w.window, softcap=w.softcap,
                                             scale=scale, out=o, lse=lse)
             self.kernel = "fwd_bf16" if w.dtype == "bf16" else "fwd_f32"
+        elif w.kind == "gqa_decode":
+            q, k, v = (inp[x].to(dev) for x in "qkv")
+            cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
+            o = torch.empty_like(q)
+            lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device=dev)
+            self.splits = mx.mxfa_decode_splitkv_gqa_num_splits(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q,
+                                                                w.heads_kv)
+            nbytes = mx.mxfa_decode_splitkv_gqa_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q,
+                                                                w.heads_kv, w.d_qk)
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+            self.call = lambda: mx.mxfa_decode_splitkv_gqa(q, k, v, cq, ck, w.seqlen_q, w.seqlen_k, causal=w.causal,
+                                                           window=w.window, softcap=w.softcap, scale=scale,
+                                                           workspace=ws, out=o, lse=lse)
+            self.kernel = "decode_gqa"
         elif w.kind == "varlen":
             q, k, v = (inp[x].to(dev) for x in "qkv")
             cq, ck = inp["cu_seqlens_q"].to(dev), inp["cu_seqlens_k"].to(dev)
@@ -254,7 +270,7 @@ def cpu_baseline(name, target_s):
         q = to_np(inp["q"]).reshape(-1, w.heads_q, w.d_qk)
         k = to_np(inp["k"]).reshape(-1, w.heads_kv, w.d_qk)
         v = to_np(inp["v"]).reshape(-1, w.heads_kv, w.d_v)
-    elif w.kind == "varlen":
+    elif w.kind in ("varlen", "gqa_decode"):
         q, k, v = to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"])
     else:
         q = to_np(inp["q"])
@@ -350,7 +366,7 @@ def main():
     names = args.workloads.split(",")
     if names == ["all"]:
         names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16",
-                 "chunked_prefill_bf16", "paged_mla_decode_bf16"]
+                 "chunked_prefill_bf16", "paged_mla_decode_bf16", "gqa_decode_bf16"]
     if PRIMARY not in names:
         names.insert(0, PRIMARY)
 
@@ -368,7 +384,7 @@ def main():
             "bytes_per_call": r.bytes,
             "kernel": r.kernel,
         }
-        if r.w.kind == "decode":
+        if r.w.kind in ("decode", "gqa_decode"):
             res["splits"] = r.splits
         results[name] = res
         print(f"[bench] {name}: {ms:.4f} ms/call, {res['tflops']:.1f} TFLOP/s, {res['gbs']:.1f} GB/s",

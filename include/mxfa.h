@@ -161,6 +161,44 @@ mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void*
                                       size_t workspace_bytes, mxfa_stream_t stream);
 
 /*
+ * Split-KV decode for standard heads with separate K and V (grouped-query
+ * attention at decode time: few query tokens per sequence). The split /
+ * combine scheme of mxfa_decode_splitkv; the query heads that share a kv head
+ * are packed into the rows of one MFMA tile (the AstrAI v1.3.9 page's
+ * split-KV MMA decode, head packing), so each kv head's keys are read once
+ * per key split for all of its query heads and tokens (up to 32 (token, head)
+ * pairs per pass).
+ *   q   [total_q, heads_q,  head_dim] bf16   k, v [total_k, heads_kv, head_dim] bf16
+ *   o   [total_q, heads_q,  head_dim] bf16   lse  [heads_q, total_q] float32 (may be NULL)
+ *   cu_seqlens_q, cu_seqlens_k as for mxfa_fwd_varlen (bottom-right causal
+ *   alignment when a sequence has fewer queries than keys).
+ * Supported: head_dim 64 or 128, bf16. Any query length is computed
+ * correctly; the kernel is meant for short ones (it re-reads the keys once
+ * per 32 (token, head) rows).
+ * num_splits: 0 picks a split count from the device's compute-unit count;
+ * otherwise 1..64. workspace: at least
+ * mxfa_decode_splitkv_gqa_workspace_bytes() bytes (0 when the plan has one
+ * split: then workspace may be NULL); owned by the caller, overwritten.
+ * Other arguments as for mxfa_fwd.
+ */
+mxfa_status mxfa_decode_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                                    int total_k, int heads_q, int heads_kv, int head_dim, int causal,
+                                    int window_left, int window_right, float softcap, float scale,
+                                    int num_splits, void* workspace, size_t workspace_bytes,
+                                    mxfa_stream_t stream);
+
+/* Workspace bytes mxfa_decode_splitkv_gqa needs (0 on error or for one split). */
+size_t mxfa_decode_splitkv_gqa_workspace_bytes(int batch, int max_seqlen_q, int max_seqlen_k,
+                                               int heads_q, int heads_kv, int head_dim,
+                                               int num_splits);
+
+/* Split count mxfa_decode_splitkv_gqa uses for these arguments (0 on error). */
+int mxfa_decode_splitkv_gqa_num_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q,
+                                       int heads_kv, int num_splits);
+
+/*
  * Workspace bytes mxfa_decode_splitkv needs for these arguments (0 when
  * nothing is needed). With num_splits = 0 it queries the current device's
  * compute-unit count (a host-side HIP query, no device work); if that fails

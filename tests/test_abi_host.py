@@ -59,6 +59,8 @@ def _ctype_of(decl: str, named: bool = True):
 def test_header_declares_the_entry_points():
     names = set(_prototypes())
     for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_decode_splitkv", "mxfa_decode_splitkv_paged",
+              "mxfa_decode_splitkv_gqa", "mxfa_decode_splitkv_gqa_workspace_bytes",
+              "mxfa_decode_splitkv_gqa_num_splits",
               "mxfa_decode_splitkv_workspace_bytes",
               "mxfa_decode_splitkv_num_splits", "mxfa_last_error", "mxfa_version"):
         assert n in names, n
@@ -167,6 +169,39 @@ def test_paged_decode_host_checks(lib, kw, status):
     assert paged(lib, **kw) == status
     if status != OK:
         assert lib.mxfa_last_error().decode()
+
+
+def gqa(lib, **kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, batch=2, mq=1, mk=100, tq=2, tk=200, hq=32, hkv=4, d=128,
+             causal=1, wl=-1, wr=-1, softcap=0.0, scale=0.09, splits=2, ws=A, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mxfa_decode_splitkv_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["batch"],
+                                       a["mq"], a["mk"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["causal"],
+                                       a["wl"], a["wr"], a["softcap"], a["scale"], a["splits"], a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(hq=30), INVALID), (dict(hkv=0), INVALID),
+    (dict(wl=-2), INVALID), (dict(softcap=-1.0), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(splits=65), INVALID), (dict(splits=-1), INVALID), (dict(ws=None), WORKSPACE),
+    (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 4), INVALID), (dict(k=None), INVALID),
+    (dict(v=A + 2), INVALID), (dict(cq=None), INVALID), (dict(mq=3), INVALID), (dict(tk=-1), INVALID),
+    (dict(batch=0), OK), (dict(tq=0, mq=0), OK),
+])
+def test_gqa_decode_host_checks(lib, kw, status):
+    assert gqa(lib, **kw) == status
+    if status != OK:
+        assert lib.mxfa_last_error().decode()
+
+
+@pytest.mark.parametrize("batch,mq,mk,hq,hkv,d,splits", [(16, 1, 2048, 32, 4, 128, 8), (3, 9, 100, 16, 2, 64, 5),
+                                                        (1, 1, 64, 8, 8, 128, 1)])
+def test_gqa_workspace_bytes_is_arithmetic(lib, batch, mq, mk, hq, hkv, d, splits):
+    groups = -(-mq * (hq // hkv) // 32)
+    want = batch * hkv * groups * splits * 32 * (d + 2) * 4 if splits > 1 else 0
+    assert mx.mxfa_decode_splitkv_gqa_workspace_bytes(batch, mq, mk, hq, hkv, d, splits) == want
+    assert mx.mxfa_decode_splitkv_gqa_num_splits(batch, mq, mk, hq, hkv, splits) == splits
 
 
 @pytest.mark.parametrize("batch,mq,mk,hq,hkv,splits", [(128, 4, 8192, 16, 1, 2), (3, 9, 100, 16, 2, 5),

@@ -316,6 +316,56 @@ def test_paged_decode_bad_page_index_touches_only_its_sequence():
             lse_ref[4:].reshape(-1), "bf16", "sequence 1")
 
 
+# ----------------------------------------------------- standard-head decode
+
+# (lens_q, lens_k, hq, hkv, d, causal, window, softcap, splits)
+GQA_CASES = [
+    ([1, 1, 1], [1, 70, 300], 32, 4, 128, False, (-1, -1), 0.0, 0),
+    ([1, 1], [2048, 129], 32, 4, 128, True, (-1, -1), 0.0, 3),
+    ([2, 4], [500, 65], 16, 2, 128, True, (100, 0), 30.0, 4),
+    ([1, 3], [700, 256], 8, 8, 64, False, (-1, -1), 0.0, 1),
+    ([5, 1, 0], [300, 0, 10], 64, 4, 128, False, (-1, -1), 0.0, 2),
+    ([1], [4096], 32, 4, 64, True, (-1, -1), 0.0, 0),
+    ([3, 2], [190, 64], 12, 3, 64, False, (17, 9), 0.0, 5),
+    ([1, 1, 1, 1], [64, 65, 127, 128], 8, 1, 128, True, (-1, -1), 5.0, 1),
+]
+
+
+def _run_gqa(p, causal, window, cap, splits, scale):
+    d = dev()
+    o, lse = mx.mxfa_decode_splitkv_gqa(p["q"].to(d), p["k"].to(d), p["v"].to(d), p["cu_seqlens_q"].to(d),
+                                        p["cu_seqlens_k"].to(d), max(p["lens_q"]), max(p["lens_k"]),
+                                        causal=causal, window=window, softcap=cap, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", GQA_CASES, ids=[f"gqa{i}" for i in range(len(GQA_CASES))])
+def test_gqa_decode_matches_oracle(case):
+    lq, lk, hq, hkv, d, causal, window, cap, splits = case
+    seed = 3500 + GQA_CASES.index(case)
+    print(f"[gqa-decode] {case} seed={seed}", flush=True)
+    p = workloads.make_problem(seed, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=lq, lens_k=lk)
+    scale = 1.0 / math.sqrt(d)
+    o_g, lse_g = _run_gqa(p, causal, window, cap, splits, scale)
+    o_ref, lse_ref, _ = oracle_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
+    compare(o_g.reshape(-1, d), lse_g.T.reshape(-1), o_ref.reshape(-1, d), lse_ref.reshape(-1), "bf16", str(case))
+
+
+def test_gqa_decode_independent_of_split_count():
+    p = workloads.make_problem(3600, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=[1, 2, 1],
+                               lens_k=[3000, 333, 64])
+    scale = 1.0 / math.sqrt(128)
+    ref_o, ref_l = _run_gqa(p, True, (-1, -1), 0.0, 1, scale)
+    for s in (2, 3, 8, 24, 64):
+        o, l = _run_gqa(p, True, (-1, -1), 0.0, s, scale)
+        assert np.abs(o - ref_o).max() <= 1e-2
+        assert np.abs(l - ref_l).max() <= 1e-4
+    o2, l2 = _run_gqa(p, True, (-1, -1), 0.0, 8, scale)
+    o3, l3 = _run_gqa(p, True, (-1, -1), 0.0, 8, scale)
+    assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
+
+
 # --------------------------------------------------- headline workloads, full size
 
 def _full_dense_or_varlen(name, n_rows):
@@ -446,3 +496,19 @@ def test_full_paged_mla_decode_bf16():
                                       head_dim_v=w.d_v, scale=w.softmax_scale)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_full_gqa_decode_bf16():
+    w = workloads.get("gqa_decode_bf16")
+    print("[full] gqa_decode_bf16: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    d = dev()
+    q, k, v = (inp[x].to(d) for x in "qkv")
+    o, lse = mx.mxfa_decode_splitkv_gqa(q, k, v, inp["cu_seqlens_q"].to(d), inp["cu_seqlens_k"].to(d), w.seqlen_q,
+                                        w.seqlen_k, causal=w.causal, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    # Every row: 16 x 32 (token, head) rows of 2048 keys each.
+    o_ref, lse_ref, _ = oracle_varlen(inp, causal=w.causal, window=w.window, softcap=w.softcap,
+                                      scale=w.softmax_scale)
+    compare(o.float().cpu().numpy().reshape(-1, w.d_v), lse.T.cpu().numpy().reshape(-1), o_ref.reshape(-1, w.d_v),
+            lse_ref.reshape(-1), "bf16", "gqa_decode_bf16")

@@ -23,6 +23,9 @@ __all__ = [
     "mxfa_fwd_varlen",
     "mxfa_decode_splitkv",
     "mxfa_decode_splitkv_paged",
+    "mxfa_decode_splitkv_gqa",
+    "mxfa_decode_splitkv_gqa_workspace_bytes",
+    "mxfa_decode_splitkv_gqa_num_splits",
     "mxfa_decode_splitkv_workspace_bytes",
     "mxfa_decode_splitkv_num_splits",
     "mxfa_version",
@@ -44,6 +47,9 @@ _SIGNATURES = {
     "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp]),
     "mxfa_decode_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_paged": (_c_int, [_vp] * 7 + [_c_int] * 14 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
+    "mxfa_decode_splitkv_gqa": (_c_int, [_vp] * 7 + [_c_int] * 11 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
+    "mxfa_decode_splitkv_gqa_workspace_bytes": (_sz, [_c_int] * 7),
+    "mxfa_decode_splitkv_gqa_num_splits": (_c_int, [_c_int] * 6),
     "mxfa_decode_splitkv_workspace_bytes": (_sz, [_c_int] * 7),
     "mxfa_decode_splitkv_num_splits": (_c_int, [_c_int] * 6),
     "mxfa_last_error": (ctypes.c_char_p, []),
@@ -285,5 +291,61 @@ def mxfa_decode_splitkv_paged(q, kv_cache, cu_seqlens_q, cache_seqlens, block_ta
                                            int(window[1]), float(softcap), _scale(scale, dqk), int(num_splits),
                                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            _stream(dev))
+    _check(st)
+    return out, lse
+
+
+def mxfa_decode_splitkv_gqa_num_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits=0) -> int:
+    s = load_library().mxfa_decode_splitkv_gqa_num_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv,
+                                                          num_splits)
+    if s <= 0:
+        raise MxfaError("mxfa: " + load_library().mxfa_last_error().decode(errors="replace"))
+    return s
+
+
+def mxfa_decode_splitkv_gqa_workspace_bytes(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, head_dim,
+                                            num_splits=0) -> int:
+    return int(load_library().mxfa_decode_splitkv_gqa_workspace_bytes(batch, max_seqlen_q, max_seqlen_k, heads_q,
+                                                                      heads_kv, head_dim, num_splits))
+
+
+def mxfa_decode_splitkv_gqa(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                            window=(-1, -1), softcap=0.0, scale=None, num_splits=0, workspace=None, out=None,
+                            lse=None, return_lse=True):
+    """Standard-head split decode: q [Tq,Hq,d], k/v [Tk,Hkv,d] bf16 (d = 64 or 128), int32 cu_seqlens.
+
+    Returns (o [Tq,Hq,d] bf16, lse [Hq,Tq] fp32). ``workspace`` is a uint8 GPU
+    tensor of at least mxfa_decode_splitkv_gqa_workspace_bytes() bytes
+    (allocated here when None and needed).
+    """
+    lib = load_library()
+    _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [T, H, d]")
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    _need(k.shape == (tk, hkv, d) and v.shape == (tk, hkv, d), "k/v shapes do not match q")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(q.dtype == torch.bfloat16, "decode supports bf16")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _need(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape, "cu_seqlens shapes differ")
+    batch = cu_seqlens_q.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(lse is None or (lse.shape == (hq, tq) and lse.dtype == torch.float32), "lse must be [Hq,Tq] fp32")
+    dev = _tensors_ok(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, workspace)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            nbytes = mxfa_decode_splitkv_gqa_workspace_bytes(batch, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
+                                                             d, num_splits)
+            if nbytes > 0:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+        ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = lib.mxfa_decode_splitkv_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                         _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
+                                         hq, hkv, d, int(bool(causal)), int(window[0]), int(window[1]),
+                                         float(softcap), _scale(scale, d), int(num_splits), _ptr(workspace),
+                                         ws_bytes, _stream(dev))
     _check(st)
     return out, lse

@@ -186,13 +186,13 @@ void decode_split_kernel(const DecodeParams p) {
     // kept out of the vector-memory count that the stage waits rely on.
     using ConstI32 = const __attribute__((address_space(4))) int32_t;
     auto page_of = [&](int kt) __attribute__((always_inline)) -> int {
-        if (!kPaged || kt >= sk) return 0;
+        if (!kPaged || kt > hi) return 0;
         const ConstI32* tab = (const ConstI32*)p.block_table;
         return tab[(long long)b * p.max_pages + kt / p.page_size];
     };
     // Buffer resource over the tile at key kt: its rows up to the last key
-    // (rows past it read as zeros). Tiles past the key range, and tiles
-    // whose page number lies outside the cache, get a resource of zero
+    // (rows past it read as zeros). Tiles past the split's last key, and
+    // tiles whose page number lies outside the cache, get a resource of zero
     // bytes: their loads return zeros without touching memory.
     auto tile_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
         long long bytes = (long long)(sk - kt - 1) * kv_tok_stride * 2 + DQK * 2;
@@ -203,7 +203,7 @@ void decode_split_kernel(const DecodeParams p) {
                 base = static_cast<const uint16_t*>(p.kv) +
                        ((long long)phys * p.page_size + kt % p.page_size) * kv_tok_stride + (long long)g * DQK;
         }
-        if (kt >= sk) bytes = 0;
+        if (kt > hi) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
         return make_rsrc(bytes ? base : KVseg, (uint32_t)bytes);
     };

@@ -126,6 +126,39 @@ size_t decode_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, i
     return (size_t)parts * (size_t)mxfa::kDecodeRows * ((size_t)head_dim_v + 2) * sizeof(float);
 }
 
+// Split plan for the standard-head decode: about two work groups per
+// compute unit (two of its 64 KB LDS rings fit one CU at head dim 128), and at
+// least two 64-key tiles per split.
+int plan_gqa_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, int heads_kv, int requested,
+                    int* err) {
+    *err = 0;
+    if (requested > 0) return requested;
+    const int group = heads_q / heads_kv;
+    const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kGqaRows - 1) / mxfa::kGqaRows;
+    const long long units = (long long)batch * heads_kv * m_groups;
+    const long long tiles = ((long long)max_seqlen_k + mxfa::kGqaTile - 1) / mxfa::kGqaTile;
+    int cus = 0;
+    int e = device_cus(&cus);
+    if (e) {
+        *err = e;
+        return 0;
+    }
+    if (units <= 0) return 1;
+    long long s = (2LL * cus + units - 1) / units;
+    if (s > tiles / 2) s = tiles / 2;
+    if (s > kMaxSplits) s = kMaxSplits;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+size_t gqa_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, int head_dim, int splits) {
+    if (splits <= 1) return 0;
+    const int group = heads_q / heads_kv;
+    const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kGqaRows - 1) / mxfa::kGqaRows;
+    const long long parts = (long long)batch * heads_kv * m_groups * splits;
+    return (size_t)parts * (size_t)mxfa::kGqaRows * ((size_t)head_dim + 2) * sizeof(float);
+}
+
 // Checks and launch shared by the contiguous (cu_k) and paged (pg) decode
 // entry points; exactly one of cu_k and pg is non-null. total_k: key rows in kv.
 mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, const int32_t* cu_seqlens_q,
@@ -360,6 +393,102 @@ mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void*
     return decode_common(q, kv_cache, o, lse, cu_seqlens_q, nullptr, &pg, batch, max_seqlen_q, max_seqlen_k,
                          total_q, num_pages * page_size, heads_q, heads_kv, head_dim_qk, head_dim_v, causal,
                          window_left, window_right, softcap, scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+int mxfa_decode_splitkv_gqa_num_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, int heads_kv,
+                                       int num_splits) {
+    g_err[0] = 0;
+    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || heads_q < 1 || heads_kv < 1 || heads_q % heads_kv ||
+        num_splits < 0 || num_splits > kMaxSplits) {
+        fail(MXFA_ERR_INVALID_ARG, "invalid decode plan arguments");
+        return 0;
+    }
+    int err = 0;
+    const int s = plan_gqa_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits, &err);
+    if (err) {
+        hip_fail((hipError_t)err, "device query for the split count");
+        return 0;
+    }
+    return s;
+}
+
+size_t mxfa_decode_splitkv_gqa_workspace_bytes(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q,
+                                               int heads_kv, int head_dim, int num_splits) {
+    const int s =
+        mxfa_decode_splitkv_gqa_num_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits);
+    if (s <= 0 || head_dim <= 0) return 0;
+    return gqa_ws_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim, s);
+}
+
+mxfa_status mxfa_decode_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int heads_q,
+                                    int heads_kv, int head_dim, int causal, int window_left, int window_right,
+                                    float softcap, float scale, int num_splits, void* workspace,
+                                    size_t workspace_bytes, mxfa_stream_t stream) {
+    g_err[0] = 0;
+    if (head_dim != 64 && head_dim != 128)
+        return fail(MXFA_ERR_UNSUPPORTED, "decode head dim %d: supported 64, 128", head_dim);
+    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+        return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
+    if (heads_kv > 0 && (long long)max_seqlen_q * (heads_q / heads_kv) > 0x7fffffffLL)
+        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen_q * heads_q / heads_kv exceeds 2^31 - 1");
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k)
+        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
+    if (num_splits < 0 || num_splits > kMaxSplits)
+        return fail(MXFA_ERR_INVALID_ARG, "num_splits must be in [0, %d]", kMaxSplits);
+    mxfa_status st = check_common(heads_q, heads_kv, window_left, window_right, softcap, scale);
+    if (st != MXFA_OK) return st;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return MXFA_OK;
+    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) != MXFA_OK) return st;
+    if ((st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)) != MXFA_OK) return st;
+    if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
+    if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
+    if (total_k > 0) {
+        if ((st = check_tensor(k, "k", 16)) != MXFA_OK) return st;
+        if ((st = check_tensor(v, "v", 16)) != MXFA_OK) return st;
+    }
+    if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+
+    int err = 0;
+    const int splits = plan_gqa_splits(batch, max_seqlen_q, max_seqlen_k, heads_q, heads_kv, num_splits, &err);
+    if (err) return hip_fail((hipError_t)err, "device query for the split count");
+    const size_t need = gqa_ws_bytes(batch, max_seqlen_q, heads_q, heads_kv, head_dim, splits);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                        workspace ? workspace_bytes : 0);
+        if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
+
+    mxfa::GqaDecodeParams p = {};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.batch = batch;
+    p.total_q = total_q;
+    p.heads_q = heads_q;
+    p.heads_kv = heads_kv;
+    p.group = heads_q / heads_kv;
+    p.m_groups = (int)(((long long)max_seqlen_q * p.group + mxfa::kGqaRows - 1) / mxfa::kGqaRows);
+    p.splits = splits;
+    if (need > 0) {
+        const long long parts = (long long)batch * heads_kv * p.m_groups * splits;
+        p.part_acc = static_cast<float*>(workspace);
+        p.part_ml = p.part_acc + parts * mxfa::kGqaRows * head_dim;
+    }
+    p.causal = causal ? 1 : 0;
+    p.window_left = window_left;
+    p.window_right = window_right;
+    p.softcap = softcap;
+    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    hipError_t e = mxfa::launch_decode_gqa(p, head_dim, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+    return MXFA_OK;
 }
 
 }  // extern "C"

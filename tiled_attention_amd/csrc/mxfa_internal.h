@@ -71,6 +71,33 @@ struct DecodeParams {
     int num_pages;               // pages in the cache (kv holds num_pages * page_size rows)
 };
 
+// Split-KV decode for standard heads (separate K and V).
+struct GqaDecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;              // may be null
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    float* part_acc;         // [batch, heads_kv, m_groups, splits, 32, head_dim] fp32 (splits > 1)
+    float* part_ml;          // [batch, heads_kv, m_groups, splits, 2, 32] fp32 (max, sum)
+    int batch;
+    int total_q;
+    int heads_q;
+    int heads_kv;
+    int group;
+    int m_groups;            // ceil(max_seqlen_q * group / 32)
+    int splits;
+    int causal;
+    int window_left;
+    int window_right;
+    float softcap;
+    float x_mul;
+    float cap_mul;
+    float cap_out;
+};
+
 // Page-table description of a paged latent cache, as the host receives it.
 struct PagedKV {
     const int32_t* block_table;
@@ -83,12 +110,16 @@ struct PagedKV {
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_gqa(const GqaDecodeParams& p, int head_dim, hipStream_t stream);
 
 // Accelerator dies (XCDs) of the device, each with its own L2.
 constexpr int kXcdCount = 8;
 
 // Rows of one decode work group: (query token, head-in-group) pairs.
 constexpr int kDecodeRows = 64;
+// Standard-head decode: rows per work group, keys per tile.
+constexpr int kGqaRows = 32;
+constexpr int kGqaTile = 64;
 // Keys per decode tile; split boundaries are multiples of it.
 constexpr int kDecodeTile = 32;
 

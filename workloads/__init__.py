@@ -46,7 +46,7 @@ class Workload:
 
     name: str
     seed: int
-    kind: str  # "dense" | "varlen" | "decode"
+    kind: str  # "dense" | "varlen" | "decode" (shared latent kv) | "gqa_decode" (separate k, v; packed)
     dtype: str  # "f32" | "bf16"
     batch: int
     heads_q: int
@@ -101,6 +101,12 @@ WORKLOADS = {
         name="chunked_prefill_bf16", seed=5, kind="dense", dtype="bf16", batch=2, heads_q=32,
         heads_kv=8, d_qk=128, d_v=128, seqlen_q=2048, seqlen_k=16384, causal=True,
         note="B=2 Hq=32 Hkv=8 Sq=2048 Sk=16384 d=128 bf16, causal (chunk after a 14336-token cache)"),
+    # Decode for standard heads: one new token per sequence, 8 query heads per
+    # kv head, separate K and V.
+    "gqa_decode_bf16": Workload(
+        name="gqa_decode_bf16", seed=7, kind="gqa_decode", dtype="bf16", batch=16, heads_q=32,
+        heads_kv=4, d_qk=128, d_v=128, seqlen_q=1, seqlen_k=2048, causal=True,
+        note="B=16, q_len 1, Hq=32 Hkv=4 d=128, kv_len 2048, bf16"),
     # The latent-KV decode above with its cache in 64-row pages, placed at
     # shuffled physical page indices.
     "paged_mla_decode_bf16": Workload(
