@@ -352,10 +352,15 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
 // Merge the splits of one (sequence, kv head, row group): M = max_s m_s,
 // w_s = exp2(m_s - M), O = sum_s w_s acc_s / sum_s w_s l_s,
 // LSE = ln2 * (M + log2 sum_s w_s l_s). One thread per (row, 4 channels).
+// The splits are read in chunks of 8 whose loads are all issued before any
+// is used (one memory round trip per chunk), merged with a running max.
+constexpr int kCombineThreads = 64;  // small groups spread the few valid rows over many CUs
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_gqa_combine_kernel(const GqaDecodeParams p) {
-    constexpr int TPR = D / 4;        // threads per row
-    constexpr int RPB = 256 / TPR;    // rows per work group
+__global__ __launch_bounds__(kCombineThreads) void decode_gqa_combine_kernel(const GqaDecodeParams p) {
+    constexpr int TPR = D / 4;                     // threads per row
+    constexpr int RPB = kCombineThreads / TPR;     // rows per work group
+    constexpr int CH = 8;             // splits per chunk
     int id = blockIdx.x;
     const int rgrp = id % (ROWS / RPB);
     id /= ROWS / RPB;
@@ -373,18 +378,33 @@ __global__ __launch_bounds__(256) void decode_gqa_combine_kernel(const GqaDecode
     const int tok = r / G;
     const int h = g * G + r % G;
     const long long pidx0 = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[(pidx0 + s) * 2 * ROWS + row]);
-    float L = 0.0f;
+    float M = -INFINITY, L = 0.0f;
     f32x4_t o = f32x4_t{};
-    if (M != -INFINITY) {
-        for (int s = 0; s < p.splits; ++s) {
-            const float* pml = p.part_ml + (pidx0 + s) * 2 * ROWS;
-            const float ws = fast_exp2(pml[row] - M);
-            L += ws * pml[ROWS + row];
-            const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p.part_acc + ((pidx0 + s) * ROWS + row) * D + d0);
-            o += ws * v;
+    for (int s0 = 0; s0 < p.splits; s0 += CH) {
+        float ms[CH], ls[CH];
+        f32x4_t as[CH];
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const bool in = s0 + j < p.splits;
+            const long long pi = pidx0 + (in ? s0 + j : 0);
+            ms[j] = in ? p.part_ml[pi * 2 * ROWS + row] : -INFINITY;
+            ls[j] = p.part_ml[pi * 2 * ROWS + ROWS + row];
+            as[j] = *reinterpret_cast<const f32x4_t*>(p.part_acc + (pi * ROWS + row) * D + d0);
         }
+        float mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ms[j]);
+        if (mc == -INFINITY) continue;  // nothing visible so far
+        const float a = fast_exp2(M - mc);  // 0 while M is -inf
+        L *= a;
+        o *= a;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float ws = fast_exp2(ms[j] - mc);  // 0 for splits past the end or with no keys
+            L += ws * ls[j];
+            o += ws * as[j];
+        }
+        M = mc;
     }
     const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
     uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * D + d0;
@@ -398,7 +418,7 @@ hipError_t launch_gqa(const GqaDecodeParams& p, hipStream_t stream) {
     const long long units = (long long)p.batch * p.heads_kv * p.m_groups;
     if (units <= 0) return hipSuccess;
     const long long grid_split = units * p.splits;
-    constexpr int RPB = 256 / (D / 4);
+    constexpr int RPB = kCombineThreads / (D / 4);
     const long long grid_comb = units * (ROWS / RPB);
     if (grid_split > 0x7fffffffLL || grid_comb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)
@@ -407,7 +427,8 @@ hipError_t launch_gqa(const GqaDecodeParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((decode_gqa_split_kernel<D, false>), dim3((unsigned)grid_split), dim3(NT), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    hipLaunchKernelGGL((decode_gqa_combine_kernel<D>), dim3((unsigned)grid_comb), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D>), dim3((unsigned)grid_comb), dim3(kCombineThreads), 0, stream,
+                       p);
     return hipGetLastError();
 }
 

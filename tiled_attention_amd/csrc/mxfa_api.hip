@@ -126,8 +126,9 @@ size_t decode_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, i
     return (size_t)parts * (size_t)mxfa::kDecodeRows * ((size_t)head_dim_v + 2) * sizeof(float);
 }
 
-// Split plan for the standard-head decode: about two work groups per
-// compute unit (two of its 64 KB LDS rings fit one CU at head dim 128), and at
+// Split plan for the standard-head decode: about one work group per compute
+// unit (two fit one CU at head dim 128, so the groups of a second round start
+// while the first finish; fewer splits also keep the combine short), and at
 // least two 64-key tiles per split.
 int plan_gqa_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, int heads_kv, int requested,
                     int* err) {
@@ -144,7 +145,7 @@ int plan_gqa_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, 
         return 0;
     }
     if (units <= 0) return 1;
-    long long s = (2LL * cus + units - 1) / units;
+    long long s = ((long long)cus + units - 1) / units;
     if (s > tiles / 2) s = tiles / 2;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s < 1) s = 1;
