@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "fwd_f32": "tiled_attention_amd/csrc/fwd_f32.hip",
     "decode_mla": "tiled_attention_amd/csrc/decode_mla.hip",
     "decode_mla_paged": "tiled_attention_amd/csrc/decode_mla.hip",
+    "decode_mla_fp8": "tiled_attention_amd/csrc/decode_mla.hip",
     "decode_gqa": "tiled_attention_amd/csrc/decode_gqa.hip",
 }
 
@@ -86,7 +87,8 @@ def work_of(w, inp):
     o_b = tq * w.heads_q * w.d_v * esz
     lse_b = tq * w.heads_q * 4
     if w.kind == "decode":
-        kv_b = tk * w.heads_kv * w.d_qk * esz  # shared latent kv, read once
+        kv_esz = 1 if w.kv_dtype == "fp8" else esz
+        kv_b = tk * w.heads_kv * w.d_qk * kv_esz  # shared latent kv, read once
     else:
         kv_b = tk * w.heads_kv * (w.d_qk + w.d_v) * esz
     return pairs, flops, q_b + kv_b + o_b + lse_b
@@ -101,8 +103,9 @@ def source_sha(name):
 # is one split kernel plus one combine kernel).
 PMC_KERNELS = {
     "fwd_bf16": ("fwd_bf16_kernel<128, 0>",),
-    "decode_mla": ("decode_split_kernel<false, false>", "decode_combine_kernel"),
-    "decode_mla_paged": ("decode_split_kernel<false, true>", "decode_combine_kernel"),
+    "decode_mla": ("decode_split_kernel<false, false, false>", "decode_combine_kernel"),
+    "decode_mla_paged": ("decode_split_kernel<false, true, false>", "decode_combine_kernel"),
+    "decode_mla_fp8": ("decode_split_kernel<false, false, true>", "decode_combine_kernel"),
     "decode_gqa": ("decode_gqa_split_kernel<128, false>", "decode_gqa_combine_kernel<128>"),
 }
 COPY_KERNEL_MARKERS = ("copyBuffer", "copy_kernel", "CopyKernel")
@@ -225,7 +228,14 @@ class Runner:
             nbytes = mx.mxfa_decode_splitkv_workspace_bytes(w.batch, w.seqlen_q, w.seqlen_k, w.heads_q,
                                                             w.heads_kv, w.d_v)
             ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-            if w.page_size:
+            if w.kv_dtype == "fp8":
+                kv8, ck = inp["kv8"].to(dev), inp["cu_seqlens_k"].to(dev)
+                kv_scale = inp["kv_scale"]
+                self.call = lambda: mx.mxfa_decode_splitkv_fp8(q, kv8, cq, ck, w.seqlen_q, w.seqlen_k, kv_scale,
+                                                               head_dim_v=w.d_v, scale=scale, workspace=ws, out=o,
+                                                               lse=lse)
+                self.kernel = "decode_mla_fp8"
+            elif w.page_size:
                 cache = inp["kv_cache"].to(dev)
                 seqlens, table = inp["cache_seqlens"].to(dev), inp["block_table"].to(dev)
                 self.call = lambda: mx.mxfa_decode_splitkv_paged(q, cache, cq, seqlens, table, w.seqlen_q,
@@ -366,7 +376,7 @@ def main():
     names = args.workloads.split(",")
     if names == ["all"]:
         names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16",
-                 "chunked_prefill_bf16", "paged_mla_decode_bf16", "gqa_decode_bf16"]
+                 "chunked_prefill_bf16", "paged_mla_decode_bf16", "gqa_decode_bf16", "mla_decode_fp8"]
     if PRIMARY not in names:
         names.insert(0, PRIMARY)
 

@@ -130,6 +130,27 @@ mxfa_status mxfa_decode_splitkv(const void* q, const void* kv, void* o, float* l
                                 size_t workspace_bytes, mxfa_stream_t stream);
 
 /*
+ * Split-KV decode over a latent cache stored as fp8 (the kernelbot
+ * amd-mixed-mla submission 588924 page names an fp8 KV; the encoding is the
+ * OCP 8-bit floating point E4M3 format) with one per-tensor scale: key row j
+ * is kv_scale * e4m3(kv8[j]) and its value the first head_dim_v channels.
+ * Same computation as mxfa_decode_splitkv on those rows; the kernel converts
+ * the codes to bf16 exactly and folds kv_scale into the score scale and the
+ * output.
+ *   kv8 [total_k, heads_kv, head_dim_qk] uint8 E4M3 codes (16-byte aligned)
+ * kv_scale: finite (scale * kv_scale too). NaN codes give NaN rows.
+ * Other arguments, the workspace and its size query as for
+ * mxfa_decode_splitkv.
+ */
+mxfa_status mxfa_decode_splitkv_fp8(const void* q, const void* kv8, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                                    int total_k, int heads_q, int heads_kv, int head_dim_qk,
+                                    int head_dim_v, int causal, int window_left, int window_right,
+                                    float softcap, float scale, float kv_scale, int num_splits,
+                                    void* workspace, size_t workspace_bytes, mxfa_stream_t stream);
+
+/*
  * Split-KV decode over a paged latent cache (the mxflashattn page's
  * flash_attn_with_kvcache interface: k/v cache of fixed-size pages, per-batch
  * cache_seqlens, block_table of page indices; the AstrAI v1.3.9 page's paged

@@ -29,7 +29,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
-F32, BF16 = 0, 1
+F32, BF16, F64 = 0, 1, 2
 
 
 class _Problem(ctypes.Structure):
@@ -88,7 +88,9 @@ def _dtype_code(a: np.ndarray) -> int:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {a.dtype}")
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs must be float32, float64 or uint16 (bf16 bits), got {a.dtype}")
 
 
 def attention_rows(q, k, v, cu_q, cu_k, *, causal=False, window=(-1, -1), softcap=0.0,
@@ -214,3 +216,42 @@ def gather_paged(kv_cache, block_table, cache_seqlens):
     else:
         kv = np.zeros((0,) + kv_cache.shape[2:], dtype=kv_cache.dtype)
     return kv, cu
+
+
+def e4m3_to_float64(codes):
+    """Values of OCP 8-bit floating point E4M3 codes (uint8), exactly, as float64.
+
+    The format of an fp8 latent cache (the kernelbot amd-mixed-mla submission
+    588924 page names fp8 KV; the encoding is the OCP 8-bit floating point
+    specification's E4M3): sign bit, 4 exponent bits with bias 7, 3 mantissa
+    bits; exponent 0 holds the subnormals m * 2^-9; the all-ones exponent is
+    an ordinary binade (up to 448) except S.1111.111, which is NaN; there
+    are no infinities.
+    """
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = sign * val
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def bf16_bits_to_float64(bits):
+    """bf16 bit patterns (uint16) as float64, exactly."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def attention_rows_fp8_latent(q, kv8, kv_scale, cu_q, cu_k, *, d_v, causal=False, window=(-1, -1), softcap=0.0,
+                              scale=None, rows=None, threads=0, lib=None):
+    """Attention over an fp8 (E4M3) shared latent cache with one per-tensor scale.
+
+    Key j's row is kv_scale * e4m3(kv8[j]) (every channel), its value the
+    first d_v channels of that row; q holds bf16 bits. The dequantised rows
+    are formed exactly in float64 and passed to ``attention_rows``.
+    """
+    kv = e4m3_to_float64(kv8) * float(kv_scale)
+    q64 = bf16_bits_to_float64(q)
+    return attention_rows(q64, kv, kv[:, :, :d_v], cu_q, cu_k, causal=causal, window=window, softcap=softcap,
+                          scale=scale, rows=rows, threads=threads, lib=lib)

@@ -43,13 +43,13 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F64 = 2 };
 
 typedef struct {
     const void* q;
     const void* k;
     const void* v;
-    int dtype;               /* ORACLE_F32 or ORACLE_BF16 (bit patterns, upcast exactly) */
+    int dtype;               /* ORACLE_F32, ORACLE_BF16 (bit patterns, upcast exactly) or ORACLE_F64 */
     int64_t q_tok_stride;    /* element strides */
     int64_t q_head_stride;
     int64_t k_tok_stride;
@@ -72,6 +72,7 @@ typedef struct {
 
 /* Exact upcast of one stored element to double. */
 static double load_elem(const void* base, int dtype, int64_t idx) {
+    if (dtype == ORACLE_F64) return ((const double*)base)[idx];
     if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
     uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
     float f;

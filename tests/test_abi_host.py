@@ -59,6 +59,7 @@ def _ctype_of(decl: str, named: bool = True):
 def test_header_declares_the_entry_points():
     names = set(_prototypes())
     for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_decode_splitkv", "mxfa_decode_splitkv_paged",
+              "mxfa_decode_splitkv_fp8",
               "mxfa_decode_splitkv_gqa", "mxfa_decode_splitkv_gqa_workspace_bytes",
               "mxfa_decode_splitkv_gqa_num_splits",
               "mxfa_decode_splitkv_workspace_bytes",
@@ -144,6 +145,28 @@ def decode(lib, **kw):
 ])
 def test_decode_host_checks(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def fp8(lib, **kw):
+    a = dict(q=A, kv=A, o=A, lse=A, cq=A, ck=A, batch=2, mq=4, mk=100, tq=8, tk=200, hq=16, hkv=1, dqk=576,
+             dv=512, causal=0, wl=-1, wr=-1, softcap=0.0, scale=0.04, kv_scale=0.01, splits=2, ws=A,
+             ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.mxfa_decode_splitkv_fp8(a["q"], a["kv"], a["o"], a["lse"], a["cq"], a["ck"], a["batch"], a["mq"],
+                                       a["mk"], a["tq"], a["tk"], a["hq"], a["hkv"], a["dqk"], a["dv"], a["causal"],
+                                       a["wl"], a["wr"], a["softcap"], a["scale"], a["kv_scale"], a["splits"],
+                                       a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_scale=float("nan")), INVALID), (dict(kv_scale=float("inf")), INVALID),
+    (dict(kv_scale=3e38, scale=10.0), INVALID), (dict(dqk=128, dv=128), UNSUPPORTED), (dict(kv=None), INVALID),
+    (dict(kv=A + 8), INVALID), (dict(ws=None), WORKSPACE), (dict(mk=300), INVALID), (dict(batch=0), OK),
+])
+def test_fp8_decode_host_checks(lib, kw, status):
+    assert fp8(lib, **kw) == status
+    if status != OK:
+        assert lib.mxfa_last_error().decode()
 
 
 def paged(lib, **kw):

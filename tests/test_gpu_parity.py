@@ -245,6 +245,68 @@ def test_decode_independent_of_split_count():
     assert np.array_equal(o2, o3) and np.array_equal(l2, l3)
 
 
+# -------------------------------------------------------- fp8 latent decode
+
+# (lens_q, lens_k, hq, hkv, causal, window, softcap, splits)
+FP8_CASES = [
+    ([1, 4, 2], [1, 70, 300], 16, 1, False, (-1, -1), 0.0, 0),
+    ([4, 3], [500, 65], 16, 1, True, (-1, -1), 0.0, 4),
+    ([4], [700], 16, 1, True, (100, 0), 30.0, 5),
+    ([9, 1], [200, 64], 16, 2, False, (-1, -1), 0.0, 2),
+    ([2, 0, 5], [64, 10, 0], 8, 1, False, (-1, -1), 0.0, 1),
+    ([4, 4], [1000, 129], 16, 1, False, (-1, -1), 0.0, 3),
+]
+
+
+def _fp8_problem(seed, lq, lk, hq, hkv, magnitude=1.0):
+    p = workloads.make_problem(seed, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    p.update(workloads.quantize_e4m3(p["kv"].float() * magnitude))
+    return p
+
+
+def _run_fp8(p, causal, window, cap, splits, scale, kv_scale=None):
+    d = dev()
+    o, lse = mx.mxfa_decode_splitkv_fp8(p["q"].to(d), p["kv8"].to(d), p["cu_seqlens_q"].to(d),
+                                        p["cu_seqlens_k"].to(d), max(p["lens_q"]), max(p["lens_k"]),
+                                        p["kv_scale"] if kv_scale is None else kv_scale, head_dim_v=512,
+                                        causal=causal, window=window, softcap=cap, scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[f"fp8-{i}" for i in range(len(FP8_CASES))])
+def test_fp8_decode_matches_oracle(case):
+    lq, lk, hq, hkv, causal, window, cap, splits = case
+    seed = 3700 + FP8_CASES.index(case)
+    print(f"[fp8-decode] {case} seed={seed}", flush=True)
+    p = _fp8_problem(seed, lq, lk, hq, hkv)
+    scale = 1.0 / math.sqrt(576)
+    o_g, lse_g = _run_fp8(p, causal, window, cap, splits, scale)
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_rows_fp8_latent(to_np(p["q"]), p["kv8"].numpy(), p["kv_scale"],
+                                                         p["cu_seqlens_q"].numpy(), p["cu_seqlens_k"].numpy(),
+                                                         d_v=512, causal=causal, window=window, softcap=cap,
+                                                         scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            str(case))
+
+
+def test_fp8_decode_equals_bf16_decode_of_dequantised_cache():
+    # With a power-of-two scale the dequantised rows are bf16 values and every
+    # step of the arithmetic matches the bf16 cache's: equal bit for bit.
+    p = _fp8_problem(3790, [4, 2], [600, 97], 16, 1)
+    kv_scale = 0.125
+    kvb = (p["kv8"].view(torch.float8_e4m3fn).float() * kv_scale).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(576)
+    print("[fp8-decode] equals bf16", flush=True)
+    o8, l8 = _run_fp8(p, True, (-1, -1), 0.0, 3, scale, kv_scale=kv_scale)
+    pb = dict(p, kv=kvb)
+    ob, lb = _run_decode(pb, 16, True, (-1, -1), 0.0, 3, scale)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+
+
 # ------------------------------------------------------- paged-cache decode
 
 # (lens_q, lens_k, hq, hkv, causal, window, softcap, splits, page_size)
@@ -512,3 +574,23 @@ def test_full_gqa_decode_bf16():
                                       scale=w.softmax_scale)
     compare(o.float().cpu().numpy().reshape(-1, w.d_v), lse.T.cpu().numpy().reshape(-1), o_ref.reshape(-1, w.d_v),
             lse_ref.reshape(-1), "bf16", "gqa_decode_bf16")
+
+
+def test_full_mla_decode_fp8():
+    w = workloads.get("mla_decode_fp8")
+    print("[full] mla_decode_fp8: generating inputs", flush=True)
+    inp = workloads.make_inputs(w)
+    d = dev()
+    o, lse = mx.mxfa_decode_splitkv_fp8(inp["q"].to(d), inp["kv8"].to(d), inp["cu_seqlens_q"].to(d),
+                                        inp["cu_seqlens_k"].to(d), w.seqlen_q, w.seqlen_k, inp["kv_scale"],
+                                        head_dim_v=w.d_v, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp["lens_q"], w.heads_q, 256, seed=w.seed)
+    import oracle
+
+    o_ref, lse_ref, _ = oracle.attention_rows_fp8_latent(to_np(inp["q"]), inp["kv8"].numpy(), inp["kv_scale"],
+                                                         inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy(),
+                                                         d_v=w.d_v, scale=w.softmax_scale, rows=rows)
+    o_c = o.float().cpu().numpy()
+    lse_c = lse.T.cpu().numpy()
+    compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "mla_decode_fp8")

@@ -360,6 +360,55 @@ def test_gather_paged_inverts_paginate(page_size, lens):
     assert cu.tolist() == [0] + np.cumsum(lens).tolist()
 
 
+# ------------------------------------------------------------ fp8 latent cache
+
+def test_e4m3_decoder_worked_values():
+    # Values fixed by the E4M3 definition (bias 7, 3 mantissa bits,
+    # subnormals m * 2^-9, S.1111.111 = NaN).
+    codes = [0x00, 0x80, 0x38, 0xB8, 0x7E, 0xFE, 0x01, 0x07, 0x08, 0x40, 0x3C, 0x77, 0x78]
+    want = [0.0, -0.0, 1.0, -1.0, 448.0, -448.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 2.0, 1.5, 240.0, 256.0]
+    got = oracle.e4m3_to_float64(codes)
+    assert got.tolist() == want
+    assert np.signbit(got[1]) and not np.signbit(got[0])
+    assert np.isnan(oracle.e4m3_to_float64([0x7F, 0xFF])).all()
+
+
+def test_e4m3_decoder_matches_torch_float8():
+    # Every code against torch's own float8_e4m3fn conversion.
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.e4m3_to_float64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+
+
+def test_float64_inputs_equal_bf16_inputs():
+    # The float64 input path reads the same values as the bf16 path.
+    q, kv, v, cq, ck = _problem(61, "bf16", 16, 1, 64, 48, [3, 4], [20, 9], shared=True)
+    o1, l1, _ = oracle.attention_rows(q, kv, v, cq, ck, causal=True)
+    q64, kv64 = oracle.bf16_bits_to_float64(q), oracle.bf16_bits_to_float64(kv)
+    o2, l2, _ = oracle.attention_rows(q64, kv64, kv64[:, :, :48], cq, ck, causal=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fp8_latent_with_power_of_two_scale_equals_bf16_cache():
+    # With a power-of-two scale every dequantised value is a bf16 value, so
+    # the fp8 path must give exactly the bf16 path's result on those values.
+    gen = torch.Generator("cpu").manual_seed(62)
+    q = torch.randn(7, 8, 64, generator=gen).to(torch.bfloat16)
+    kv8 = (torch.randn(30, 1, 64, generator=gen) * 8).to(torch.float8_e4m3fn)
+    kvb = (kv8.to(torch.float32) * 0.25).to(torch.bfloat16)
+    cq = np.array([0, 3, 7], dtype=np.int32)
+    ck = np.array([0, 12, 30], dtype=np.int32)
+    bits = workloads.to_numpy_bits
+    o1, l1, _ = oracle.attention_rows_fp8_latent(bits(q), kv8.view(torch.uint8).numpy(), 0.25, cq, ck, d_v=48,
+                                                 causal=True, scale=0.125)
+    kvn = bits(kvb)
+    o2, l2, _ = oracle.attention_rows(bits(q), kvn, kvn[:, :, :48], cq, ck, causal=True, scale=0.125)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 # ----------------------------------------------------------- planted mistakes
 
 MUTANTS = {

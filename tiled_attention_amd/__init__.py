@@ -23,6 +23,7 @@ __all__ = [
     "mxfa_fwd_varlen",
     "mxfa_decode_splitkv",
     "mxfa_decode_splitkv_paged",
+    "mxfa_decode_splitkv_fp8",
     "mxfa_decode_splitkv_gqa",
     "mxfa_decode_splitkv_gqa_workspace_bytes",
     "mxfa_decode_splitkv_gqa_num_splits",
@@ -47,6 +48,7 @@ _SIGNATURES = {
     "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp]),
     "mxfa_decode_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_paged": (_c_int, [_vp] * 7 + [_c_int] * 14 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
+    "mxfa_decode_splitkv_fp8": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float] * 3 + [_c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_gqa": (_c_int, [_vp] * 7 + [_c_int] * 11 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_gqa_workspace_bytes": (_sz, [_c_int] * 7),
     "mxfa_decode_splitkv_gqa_num_splits": (_c_int, [_c_int] * 6),
@@ -347,5 +349,45 @@ def mxfa_decode_splitkv_gqa(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, m
                                          hq, hkv, d, int(bool(causal)), int(window[0]), int(window[1]),
                                          float(softcap), _scale(scale, d), int(num_splits), _ptr(workspace),
                                          ws_bytes, _stream(dev))
+    _check(st)
+    return out, lse
+
+
+def mxfa_decode_splitkv_fp8(q, kv8, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, kv_scale, *,
+                            head_dim_v=512, causal=False, window=(-1, -1), softcap=0.0, scale=None, num_splits=0,
+                            workspace=None, out=None, lse=None, return_lse=True):
+    """Latent-KV split decode over an fp8 cache: q [Tq,Hq,576] bf16; kv8 [Tk,Hkv,576] OCP e4m3 codes
+    (uint8 or torch.float8_e4m3fn); key rows are kv_scale * kv8, values their first head_dim_v channels.
+
+    Returns (o [Tq,Hq,head_dim_v] bf16, lse [Hq,Tq] fp32); workspace as for mxfa_decode_splitkv.
+    """
+    lib = load_library()
+    _need(q.dim() == 3 and kv8.dim() == 3, "q and kv8 must be [T, H, d]")
+    _need(kv8.dtype in (torch.uint8, torch.float8_e4m3fn), "kv8 must hold e4m3 codes (uint8 or float8_e4m3fn)")
+    tq, hq, dqk = q.shape
+    tk, hkv = kv8.shape[0], kv8.shape[1]
+    _need(kv8.shape[2] == dqk, "q and kv8 head dims differ")
+    _need(q.dtype == torch.bfloat16, "q must be bf16")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _need(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape, "cu_seqlens shapes differ")
+    batch = cu_seqlens_q.shape[0] - 1
+    if out is None:
+        out = torch.empty((tq, hq, head_dim_v), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need(out.shape == (tq, hq, head_dim_v) and out.dtype == q.dtype, "out must be [Tq,Hq,head_dim_v]")
+    _need(lse is None or (lse.shape == (hq, tq) and lse.dtype == torch.float32), "lse must be [Hq,Tq] fp32")
+    dev = _tensors_ok(q, kv8, out, lse, cu_seqlens_q, cu_seqlens_k, workspace)
+    with torch.cuda.device(dev):
+        if workspace is None:
+            nbytes = mxfa_decode_splitkv_workspace_bytes(batch, int(max_seqlen_q), int(max_seqlen_k), hq, hkv,
+                                                         head_dim_v, num_splits)
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        st = lib.mxfa_decode_splitkv_fp8(_ptr(q), _ptr(kv8), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                         _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
+                                         hq, hkv, dqk, int(head_dim_v), int(bool(causal)), int(window[0]),
+                                         int(window[1]), float(softcap), _scale(scale, dqk), float(kv_scale),
+                                         int(num_splits), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st)
     return out, lse

@@ -58,9 +58,15 @@ static_assert(LOADS * 16 * NTHREADS == TILEB, "tile must split into whole loads"
 // (transposing V reads).
 MXFA_DEV int swz(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
-template <bool kCap, bool kPaged>
+// fp8 latent rows: 16-byte chunks per row, chunks per thread per tile.
+constexpr int CPR8 = DQK / 16;                                // 36
+constexpr int LOADS8 = (BN * CPR8 + NTHREADS - 1) / NTHREADS;  // 5 (the last for half the threads)
+
+template <bool kCap, bool kPaged, bool kFp8>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_split_kernel(const DecodeParams p) {
+    static_assert(!(kPaged && kFp8), "the fp8 cache is contiguous");
+    constexpr int ESZ = kFp8 ? 1 : 2;  // bytes per stored kv element
     // Five LDS objects: a reader of one stage then never waits for the loads
     // streaming into the others.
     __shared__ __attribute__((aligned(1024))) char sT0[TILEB];
@@ -177,7 +183,7 @@ void decode_split_kernel(const DecodeParams p) {
         const int c = (P % CPR) ^ swz(row);
         return (uint32_t)(row * (int)(kv_tok_stride * 2) + c * 16);
     };
-    const uint16_t* KVseg = static_cast<const uint16_t*>(p.kv) + (long long)k_start * kv_tok_stride + (long long)g * DQK;
+    const char* KVseg = static_cast<const char*>(p.kv) + ((long long)k_start * kv_tok_stride + (long long)g * DQK) * ESZ;
     // Paged cache: physical page of the tile at key kt (a tile never
     // straddles a page, pages holding a multiple of BN keys); 0 for tiles
     // past the keys, which are never read. Read one step before its use.
@@ -195,13 +201,13 @@ void decode_split_kernel(const DecodeParams p) {
     // tiles whose page number lies outside the cache, get a resource of zero
     // bytes: their loads return zeros without touching memory.
     auto tile_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
-        long long bytes = (long long)(sk - kt - 1) * kv_tok_stride * 2 + DQK * 2;
-        const uint16_t* base = KVseg + (long long)kt * kv_tok_stride;
+        long long bytes = ((long long)(sk - kt - 1) * kv_tok_stride + DQK) * ESZ;
+        const char* base = KVseg + (long long)kt * kv_tok_stride * ESZ;
         if (kPaged) {
             if ((unsigned)phys >= (unsigned)p.num_pages) bytes = 0;
             else
-                base = static_cast<const uint16_t*>(p.kv) +
-                       ((long long)phys * p.page_size + kt % p.page_size) * kv_tok_stride + (long long)g * DQK;
+                base = static_cast<const char*>(p.kv) +
+                       (((long long)phys * p.page_size + kt % p.page_size) * kv_tok_stride + (long long)g * DQK) * ESZ;
         }
         if (kt > hi) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
@@ -216,6 +222,52 @@ void decode_split_kernel(const DecodeParams p) {
     };
     auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) {
         issue_part(tile_rsrc(kt, page_of(kt)), stage, 0, LOADS);
+    };
+    // fp8 rows take another way into LDS: 16-byte chunks (16 values) are
+    // loaded into registers four tiles ahead, converted to bf16 (exact: every
+    // e4m3 value is a bf16 value) and written into the same swizzled bf16
+    // stages. Chunk P = n*256 + tid of a tile is row P / 36, chunk P % 36,
+    // whose values are the bf16 logical chunks 2c and 2c + 1 of the row (at
+    // LDS offsets lo8[n] and lo8[n] ^ 16: the swizzle keeps the pair in one
+    // aligned 32-byte slot). Positions past the tile (n = 4, tid >= 128)
+    // reload chunk tid and are not written.
+    uint32_t go8[LOADS8], lo8[LOADS8];
+    if constexpr (kFp8) {
+#pragma unroll
+        for (int n = 0; n < LOADS8; ++n) {
+            int P = n * NTHREADS + tid;
+            if (P >= BN * CPR8) P = tid;
+            const int row = P / CPR8;
+            const int c = P % CPR8;
+            go8[n] = (uint32_t)(row * (int)kv_tok_stride + c * 16);
+            lo8[n] = (uint32_t)(row * ROWB + (((2 * c) ^ swz(row)) << 4));
+        }
+    }
+    struct Raw8 {
+        u32x4_t v[LOADS8];
+    };
+    auto load8 = [&](int kt, Raw8& r) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt, 0);
+#pragma unroll
+        for (int n = 0; n < LOADS8; ++n) r.v[n] = buffer_load16(rs, go8[n], 0);
+    };
+    auto store8 = [&](const Raw8& r, char* stage) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < LOADS8; ++n) {
+            if (n == LOADS8 - 1 && tid >= BN * CPR8 - (LOADS8 - 1) * NTHREADS) break;
+            uint32_t h[8];
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+                const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[n][wd], false);
+                const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[n][wd], true);
+                // bf16 = the high half of the float (exact here).
+                h[2 * wd] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+                h[2 * wd + 1] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+            }
+            typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+            *(lds_u32x4*)to_lds(stage + lo8[n]) = u32x4_t{h[0], h[1], h[2], h[3]};
+            *(lds_u32x4*)to_lds(stage + (lo8[n] ^ 16u)) = u32x4_t{h[4], h[5], h[6], h[7]};
+        }
     };
 
     // O^T accumulators: channel block cb (channels 256*ch + 32*cb + ...), column lr.
@@ -368,6 +420,7 @@ void decode_split_kernel(const DecodeParams p) {
             for (int q4 = 0; q4 < 4; ++q4)
                 sS[w][q4][lane] = f32x4_t{s_mine[4 * q4], s_mine[4 * q4 + 1], s_mine[4 * q4 + 2], s_mine[4 * q4 + 3]};
         };
+      if constexpr (!kFp8) {
         issue_tile(kt0, sT0);
         issue_tile(kt0 + BN, sT1);
         issue_tile(kt0 + 2 * BN, sT2);
@@ -438,6 +491,64 @@ void decode_split_kernel(const DecodeParams p) {
         if (j + 2 < ntiles) step(st2{}, j + 2);
         // Drain the look-ahead loads before the work group's LDS is released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        // fp8 rows: tile j is loaded into registers in step j-4 (set j % 4)
+        // and converted into its LDS stage j % 4 at the end of step j-2.
+        Raw8 R0, R1, R2, R3;
+        load8(kt0, R0);
+        load8(kt0 + BN, R1);
+        load8(kt0 + 2 * BN, R2);
+        load8(kt0 + 3 * BN, R3);
+        store8(R0, sT0);
+        store8(R1, sT1);
+        lds_barrier();
+        if (block_active) {
+            s_mine = qk_tile(sT0);
+            publish();
+        }
+        lds_barrier();
+        // Step j: loads of tile j+4 into the registers of tile j (converted in
+        // step j-2); scores of tile j+1 with the softmax of tile j; barrier;
+        // publish, P V of tile j; tile j+2 converted into the stage of tile
+        // j-2 (last read in step j-2); barrier.
+        auto step8 = [&](auto stage_tag, int j, Raw8& rl, const Raw8& rc) __attribute__((always_inline)) {
+            constexpr int S = decltype(stage_tag)::value;
+            char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : S == 2 ? sT2 : sT3;
+            char* const nxt = S == 0 ? sT1 : S == 1 ? sT2 : S == 2 ? sT3 : sT0;
+            char* const fill = S == 0 ? sT2 : S == 1 ? sT3 : S == 2 ? sT0 : sT1;
+            uint32_t pk[8];
+            float alpha = 1.0f;
+            load8(kt0 + (j + 4) * BN, rl);
+            if (block_active)
+                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, []() __attribute__((always_inline)) {});
+            lds_barrier();
+            if (block_active) {
+                if (j + 1 < ntiles) publish();
+                if (wave_any(alpha != 1.0f)) {
+#pragma unroll
+                    for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
+                }
+                pv_tile(cur, pk);
+            }
+            store8(rc, fill);
+            lds_barrier();
+        };
+        using st0 = std::integral_constant<int, 0>;
+        using st1 = std::integral_constant<int, 1>;
+        using st2 = std::integral_constant<int, 2>;
+        using st3 = std::integral_constant<int, 3>;
+        int j = 0;
+        for (; j + STAGES <= ntiles; j += STAGES) {
+            step8(st0{}, j, R0, R2);
+            step8(st1{}, j + 1, R1, R3);
+            step8(st2{}, j + 2, R2, R0);
+            step8(st3{}, j + 3, R3, R1);
+        }
+        if (j < ntiles) step8(st0{}, j, R0, R2);
+        if (j + 1 < ntiles) step8(st1{}, j + 1, R1, R3);
+        if (j + 2 < ntiles) step8(st2{}, j + 2, R2, R0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
     }
 
     // Partial (m, l, acc) of this split: row 32*rb + lr of the group, channels
@@ -504,7 +615,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
             }
         }
     }
-    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    const float inv = (L > 0.0f) ? p.v_scale / L : 0.0f;  // v_scale: the fp8 cache's dequantisation scale
     uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * DV + d0;
     u32x4_t v0, v1;
 #pragma unroll
@@ -527,12 +638,15 @@ hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream) {
     if (grid_split > 0x7fffffffLL || units * (ROWS / CROWS) > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)grid_split);
     const bool cap = p.softcap > 0.0f;
-    if (p.block_table) {
-        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, dim3(NTHREADS), 0, stream, p);
-        else hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, dim3(NTHREADS), 0, stream, p);
+    if (p.kv_fp8) {
+        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, false, true>), grid, dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<false, false, true>), grid, dim3(NTHREADS), 0, stream, p);
+    } else if (p.block_table) {
+        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, true, false>), grid, dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<false, true, false>), grid, dim3(NTHREADS), 0, stream, p);
     } else {
-        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, dim3(NTHREADS), 0, stream, p);
-        else hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, dim3(NTHREADS), 0, stream, p);
+        if (cap) hipLaunchKernelGGL((decode_split_kernel<true, false, false>), grid, dim3(NTHREADS), 0, stream, p);
+        else hipLaunchKernelGGL((decode_split_kernel<false, false, false>), grid, dim3(NTHREADS), 0, stream, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

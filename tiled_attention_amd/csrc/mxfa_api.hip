@@ -162,11 +162,13 @@ size_t gqa_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, int 
 
 // Checks and launch shared by the contiguous (cu_k) and paged (pg) decode
 // entry points; exactly one of cu_k and pg is non-null. total_k: key rows in kv.
+// kv_fp8: kv holds OCP e4m3 values standing for kv_scale times themselves.
 mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, const int32_t* cu_seqlens_q,
                           const int32_t* cu_seqlens_k, const mxfa::PagedKV* pg, int batch, int max_seqlen_q,
                           int max_seqlen_k, int total_q, int total_k, int heads_q, int heads_kv, int head_dim_qk,
                           int head_dim_v, int causal, int window_left, int window_right, float softcap, float scale,
-                          int num_splits, void* workspace, size_t workspace_bytes, mxfa_stream_t stream) {
+                          int num_splits, void* workspace, size_t workspace_bytes, mxfa_stream_t stream,
+                          int kv_fp8 = 0, float kv_scale = 1.0f) {
     if (head_dim_qk != 576 || head_dim_v != 512)
         return fail(MXFA_ERR_UNSUPPORTED, "decode head dims (%d, %d): supported (576, 512)", head_dim_qk, head_dim_v);
     if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
@@ -187,6 +189,8 @@ mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, co
     if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
     if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
     if (total_k > 0 && (st = check_tensor(kv, "kv", 16)) != MXFA_OK) return st;
+    if (kv_fp8 && (heads_kv * (long long)head_dim_qk) % 16)
+        return fail(MXFA_ERR_INVALID_ARG, "fp8 kv rows must be a multiple of 16 bytes");
     if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
 
     int err = 0;
@@ -220,7 +224,10 @@ mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, co
     p.window_left = window_left;
     p.window_right = window_right;
     p.softcap = softcap;
-    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    // The scores of an fp8 cache carry its scale: fold it into the score scale.
+    fill_scaling(scale * kv_scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    p.kv_fp8 = kv_fp8;
+    p.v_scale = kv_scale;
     if (pg) {
         p.block_table = pg->block_table;
         p.seqlens_k = pg->seqlens;
@@ -370,6 +377,22 @@ mxfa_status mxfa_decode_splitkv(const void* q, const void* kv, void* o, float* l
     return decode_common(q, kv, o, lse, cu_seqlens_q, cu_seqlens_k, nullptr, batch, max_seqlen_q, max_seqlen_k,
                          total_q, total_k, heads_q, heads_kv, head_dim_qk, head_dim_v, causal, window_left,
                          window_right, softcap, scale, num_splits, workspace, workspace_bytes, stream);
+}
+
+mxfa_status mxfa_decode_splitkv_fp8(const void* q, const void* kv8, void* o, float* lse, const int32_t* cu_seqlens_q,
+                                    const int32_t* cu_seqlens_k, int batch, int max_seqlen_q, int max_seqlen_k,
+                                    int total_q, int total_k, int heads_q, int heads_kv, int head_dim_qk,
+                                    int head_dim_v, int causal, int window_left, int window_right, float softcap,
+                                    float scale, float kv_scale, int num_splits, void* workspace,
+                                    size_t workspace_bytes, mxfa_stream_t stream) {
+    g_err[0] = 0;
+    if (total_k < 0) return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
+    if (max_seqlen_k > total_k) return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
+    if (!isfinite(kv_scale) || !isfinite(scale * kv_scale))
+        return fail(MXFA_ERR_INVALID_ARG, "kv_scale (and scale * kv_scale) must be finite");
+    return decode_common(q, kv8, o, lse, cu_seqlens_q, cu_seqlens_k, nullptr, batch, max_seqlen_q, max_seqlen_k,
+                         total_q, total_k, heads_q, heads_kv, head_dim_qk, head_dim_v, causal, window_left,
+                         window_right, softcap, scale, num_splits, workspace, workspace_bytes, stream, 1, kv_scale);
 }
 
 mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void* o, float* lse,

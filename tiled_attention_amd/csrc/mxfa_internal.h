@@ -69,6 +69,10 @@ struct DecodeParams {
     int page_size;               // keys per page, a multiple of kDecodeTile
     int max_pages;               // row length of block_table
     int num_pages;               // pages in the cache (kv holds num_pages * page_size rows)
+    // fp8 (OCP e4m3) latent cache: stored value x stands for v_scale * x; the
+    // scale of the scores is folded into x_mul / cap_mul by the host.
+    int kv_fp8;
+    float v_scale;               // 1 for a bf16 cache
 };
 
 // Split-KV decode for standard heads (separate K and V).

@@ -11,8 +11,10 @@ Recipe (the same for every workload):
   k, then v -- or q then the shared latent kv for the latent-KV decode, then
   (paged cache only) one permutation of the physical page indices;
 * values are float32 ``randn`` (N(0, 1)); bf16 workloads cast them with
-  round-to-nearest-even (torch's ``.to(torch.bfloat16)``). The stored,
-  already-rounded tensors are the inputs to both sides of every comparison.
+  round-to-nearest-even (torch's ``.to(torch.bfloat16)``); an fp8 latent
+  cache holds the E4M3 codes of kv / scale with scale = amax / 448
+  (``quantize_e4m3``). The stored, already-rounded tensors are the inputs to
+  both sides of every comparison.
 
 Layouts: dense ``[B, S, H, d]``; packed (varlen) ``[total, H, d]`` with int32
 ``cu_seqlens`` of length ``batch + 1`` starting at 0; latent-KV decode keeps a
@@ -35,6 +37,7 @@ __all__ = [
     "make_inputs",
     "make_problem",
     "paginate",
+    "quantize_e4m3",
     "varlen_lengths",
     "to_numpy_bits",
 ]
@@ -62,6 +65,7 @@ class Workload:
     softcap: float = 0.0
     scale: Optional[float] = None  # None -> d_qk ** -0.5
     page_size: int = 0  # decode: > 0 stores the latent kv in a paged cache of this many rows per page
+    kv_dtype: str = ""  # decode: "fp8" stores the latent kv as OCP e4m3 codes with one per-tensor scale
     note: str = field(default="", compare=False)
 
     @property
@@ -101,6 +105,12 @@ WORKLOADS = {
         name="chunked_prefill_bf16", seed=5, kind="dense", dtype="bf16", batch=2, heads_q=32,
         heads_kv=8, d_qk=128, d_v=128, seqlen_q=2048, seqlen_k=16384, causal=True,
         note="B=2 Hq=32 Hkv=8 Sq=2048 Sk=16384 d=128 bf16, causal (chunk after a 14336-token cache)"),
+    # The latent-KV decode above with the cache in fp8 (e4m3) and one scale.
+    "mla_decode_fp8": Workload(
+        name="mla_decode_fp8", seed=8, kind="decode", dtype="bf16", batch=128, heads_q=16,
+        heads_kv=1, d_qk=576, d_v=512, seqlen_q=4, seqlen_k=8192, causal=False,
+        scale=1.0 / math.sqrt(576), kv_dtype="fp8",
+        note="mla_decode_bf16's shapes, latent kv as e4m3 codes with a per-tensor scale"),
     # Decode for standard heads: one new token per sequence, 8 query heads per
     # kv head, separate K and V.
     "gqa_decode_bf16": Workload(
@@ -218,6 +228,17 @@ def paginate(kv: torch.Tensor, lens_k, page_size: int, gen: torch.Generator, *, 
     return {"kv_cache": cache, "block_table": table, "cache_seqlens": torch.tensor(lens, dtype=torch.int32)}
 
 
+def quantize_e4m3(x: torch.Tensor) -> dict:
+    """Input preparation for an fp8 cache: one per-tensor scale, amax / 448
+    (448 is the largest E4M3 value), and the codes of x / scale rounded to
+    nearest-even by torch's float8_e4m3fn conversion. Returns ``kv8`` (uint8
+    codes, same shape) and ``kv_scale`` (a Python float, exactly a float32)."""
+    amax = float(x.abs().max()) if x.numel() else 1.0
+    scale = float(torch.tensor(amax / 448.0 if amax > 0 else 1.0, dtype=torch.float32))
+    codes = (x.to(torch.float32) / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return {"kv8": codes, "kv_scale": scale}
+
+
 def make_inputs(w: Workload) -> dict:
     """The inputs of workload ``w`` (see the module docstring for the recipe)."""
     gen = torch.Generator("cpu").manual_seed(int(w.seed))
@@ -230,7 +251,9 @@ def make_inputs(w: Workload) -> dict:
     tq, tk = sum(lens_q), sum(lens_k)
     out = {"lens_q": lens_q, "lens_k": lens_k, "cu_seqlens_q": _cu(lens_q), "cu_seqlens_k": _cu(lens_k)}
     out["q"] = _draw(gen, (tq, w.heads_q, w.d_qk), w.dtype)
-    if w.kind == "decode":
+    if w.kind == "decode" and w.kv_dtype == "fp8":
+        out.update(quantize_e4m3(_draw(gen, (tk, w.heads_kv, w.d_qk), "f32")))
+    elif w.kind == "decode":
         out["kv"] = _draw(gen, (tk, w.heads_kv, w.d_qk), w.dtype)
         if w.page_size:
             out.update(paginate(out["kv"], lens_k, w.page_size, gen))
