@@ -409,6 +409,56 @@ def test_fp8_latent_with_power_of_two_scale_equals_bf16_cache():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+# Planted mistakes in the Python-side oracle functions: each mutant is a copy
+# of the function's source with one plausible error, and each must fail one
+# of the pins above.
+PY_MUTANTS = {
+    "gather_row_page_swapped": ("gather_paged", "rows.append(kv_cache[page, j % page_size])",
+                                "rows.append(kv_cache[page, j // page_size])"),
+    "gather_page_index_off": ("gather_paged", "logical = j // page_size", "logical = (j + 1) // page_size"),
+    "gather_table_transposed": ("gather_paged", "page = int(table[b, logical])", "page = int(table[logical % table.shape[0], b % table.shape[1]])"),
+    "e4m3_bias_8": ("e4m3_to_float64", "np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
+    "e4m3_subnormal_scale": ("e4m3_to_float64", "m * 2.0 ** -9", "m * 2.0 ** -10"),
+    "e4m3_no_nan": ("e4m3_to_float64", "(e == 15) & (m == 7)", "(e == 16) & (m == 7)"),
+    "e4m3_mantissa_4bits": ("e4m3_to_float64", "(1.0 + m / 8.0)", "(1.0 + m / 16.0)"),
+}
+
+
+def _python_pins_fail(name, fn) -> bool:
+    saved = getattr(oracle, name)
+    setattr(oracle, name, fn)
+    try:
+        checks = ([test_gather_paged_worked_example, test_gather_paged_rejects_bad_pages]
+                  + [lambda ps=ps, ls=ls: test_gather_paged_inverts_paginate(ps, ls)
+                     for ps, ls in [(32, [1, 70, 300]), (64, [64, 0, 128])]]
+                  + [test_e4m3_decoder_worked_values, test_e4m3_decoder_matches_torch_float8])
+        for chk in checks:
+            try:
+                chk()
+            except (AssertionError, ValueError, IndexError, pytest.fail.Exception):
+                return True
+        return False
+    finally:
+        setattr(oracle, name, saved)
+
+
+@pytest.mark.parametrize("mutant", sorted(PY_MUTANTS))
+def test_planted_python_mistake_fails_a_pin(mutant):
+    import inspect
+    import textwrap
+    name, before, after = PY_MUTANTS[mutant]
+    src = textwrap.dedent(inspect.getsource(getattr(oracle, name)))
+    assert src.count(before) == 1, f"mutation site for {mutant} not found exactly once"
+    ns = {"np": np}
+    exec(compile(src.replace(before, after), f"<mutant {mutant}>", "exec"), ns)
+    assert _python_pins_fail(name, ns[name]), f"planted mistake {mutant} passed every pin"
+
+
+def test_unmutated_python_oracle_passes_pins():
+    for name in ("gather_paged", "e4m3_to_float64"):
+        assert not _python_pins_fail(name, getattr(oracle, name))
+
+
 # ----------------------------------------------------------- planted mistakes
 
 MUTANTS = {
