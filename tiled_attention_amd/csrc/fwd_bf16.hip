@@ -413,15 +413,19 @@ void fwd_bf16_kernel(const FwdParams p) {
         issue(Kseg, kt0, sK0);
         issue(Vseg, kt0, sV0);
         issue(Kseg, kt0 + BN, sK1);  // zero-byte past the end
-        // Q and K0 are all tile 0's scores need (V0 and K1 may still run);
-        // the first step's closing wait covers the rest.
+        // Q and K0 are all tile 0's scores need (V0 and K1 may still run).
         asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * LOADS) : "memory");
         lds_barrier();
         f32x16_t sa[2], sb[2];
         float mt_a = -INFINITY, mt_b = -INFINITY;
         qk(sa, sK0, [] {});
         mt_a = tile_full(kt0) ? logits_max(std::false_type{}, sa, kt0) : logits_max(std::true_type{}, sa, kt0);
-        lds_barrier();  // every wave is done with K0 before K2 overwrites it
+        // The first step reads K1 and V0. Each of them is loaded by all four
+        // waves, and a wave's own wait covers only its own part: wait for all
+        // of this wave's loads, then the barrier covers the other waves'
+        // parts (and ends every wave's use of K0 before K2 overwrites it).
+        wait_vmem();
+        lds_barrier();
 
         // Tile j (parity P = j % 2): S_j in s_cur (masked, max mt_cur); K(j+1)
         // in sK[1-P] and V(j) in sV[P] are resident; K(j+2) goes to sK[P] and
