@@ -499,6 +499,36 @@ def test_full_chunked_prefill_bf16():
     _full_dense_or_varlen("chunked_prefill_bf16", 384)
 
 
+def test_prefill_after_kernels_that_leave_other_data_in_lds():
+    # Regression: a tile is loaded into LDS by all waves of a work group, and a
+    # wave's own wait covers only its part, so every read of a tile must come
+    # after a barrier that follows every wave's wait. A read that came too
+    # early picked up what the previous kernel on that CU left in LDS. The
+    # standard-head decode leaves fp32 partials there (whose low halves are
+    # arbitrary bf16 patterns, NaN included); the prefill right after it must
+    # still give finite, correct rows everywhere.
+    w = workloads.get("varlen_gqa_causal_bf16")
+    inp = workloads.make_inputs(w)
+    d = dev()
+    q, k, v = (inp[x].to(d) for x in "qkv")
+    cq, ck = inp["cu_seqlens_q"].to(d), inp["cu_seqlens_k"].to(d)
+    gp = workloads.make_problem(3610, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=[1] * 64,
+                                lens_k=[1024] * 64)
+    gq, gk, gv = (gp[x].to(d) for x in "qkv")
+    gcq, gck = gp["cu_seqlens_q"].to(d), gp["cu_seqlens_k"].to(d)
+    ref = None
+    for rep in range(3):
+        print(f"[lds-reuse] round {rep}", flush=True)
+        mx.mxfa_decode_splitkv_gqa(gq, gk, gv, gcq, gck, 1, 1024, num_splits=8)
+        o, lse = mx.mxfa_fwd_varlen(q, k, v, cq, ck, max(inp["lens_q"]), max(inp["lens_k"]), causal=True)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(lse).all()) and bool(torch.isfinite(o.float()).all())
+        if ref is None:
+            ref = (o.clone(), lse.clone())
+        else:
+            assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
 def test_full_mla_decode_bf16():
     w = workloads.get("mla_decode_bf16")
     print("[full] mla_decode_bf16: generating inputs", flush=True)
