@@ -106,7 +106,7 @@ PMC_KERNELS = {
     "decode_mla": ("decode_split_kernel<false, false, false>", "decode_combine_kernel"),
     "decode_mla_paged": ("decode_split_kernel<false, true, false>", "decode_combine_kernel"),
     "decode_mla_fp8": ("decode_split_kernel<false, false, true>", "decode_combine_kernel"),
-    "decode_gqa": ("decode_gqa_split_kernel<128, false>",),
+    "decode_gqa": ("decode_gqa_split_kernel<128, false>", "decode_gqa_combine_kernel<128>"),
 }
 COPY_KERNEL_MARKERS = ("copyBuffer", "copy_kernel", "CopyKernel")
 

@@ -199,12 +199,7 @@ mxfa_status mxfa_decode_splitkv_paged(const void* q, const void* kv_cache, void*
  * num_splits: 0 picks a split count from the device's compute-unit count;
  * otherwise 1..64. workspace: at least
  * mxfa_decode_splitkv_gqa_workspace_bytes() bytes (0 when the plan has one
- * split: then workspace may be NULL); owned by the caller. It holds the split
- * partials and, at its end, one 8-byte arrival counter per (sequence, kv
- * head, 32-row group): the last split to finish merges the partials. The
- * counters need no initialisation (each call tags them with its own epoch and
- * the last arrival clears them), but two calls in flight at the same time on
- * one workspace race.
+ * split: then workspace may be NULL); owned by the caller, overwritten.
  * Other arguments as for mxfa_fwd.
  */
 mxfa_status mxfa_decode_splitkv_gqa(const void* q, const void* k, const void* v, void* o, float* lse,

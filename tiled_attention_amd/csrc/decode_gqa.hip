@@ -19,9 +19,8 @@
 //   operand comes from ds_read_b64_tr_b16 in the matching key order).
 // Each wave keeps its own running (max, sum, accumulator); at the end the two
 // are merged through LDS. With one split the work group writes O and the LSE
-// itself; otherwise it writes the split's partial and arrives on a per-unit
-// counter, and the last split to arrive merges all of them (the combine fused
-// into the last-arriving split, as the kernelbot page's reduction could be).
+// itself; otherwise it writes the split's partial and a combine kernel (one
+// thread per row and 4 channels) merges the splits.
 //
 // The rows hold at most 32 valid (token, head) pairs and usually 8 (one token,
 // a group of 8): the MFMAs do up to 4x more work than needed, which costs
@@ -299,136 +298,119 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
         L = sML[0][1][lr] * fast_exp2(m0 - M) + sML[1][1][lr] * fast_exp2(m1 - M);
         f_mine = fast_exp2(m_run - M);
     }
-    // Each wave keeps half of the output blocks (HB of them, blocks
-    // HB*w .. HB*w + HB - 1) and takes the partner's share of those through
-    // LDS. The rest of the tail is written once per half so that every
-    // accumulator index is a compile-time constant.
-    constexpr int HB = DBLK / 2;
     f32x4_t* const xbuf = reinterpret_cast<f32x4_t*>(sK0);  // [DBLK][4][64] float4
+    if (w == 1) {
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-        if (db / HB == w) continue;
+        for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-            xbuf[(db * 4 + q4) * 64 + lane] = f32x4_t{acc[db][4 * q4] * f_mine, acc[db][4 * q4 + 1] * f_mine,
-                                                      acc[db][4 * q4 + 2] * f_mine, acc[db][4 * q4 + 3] * f_mine};
+            for (int q4 = 0; q4 < 4; ++q4)
+                xbuf[(db * 4 + q4) * 64 + lane] = f32x4_t{acc[db][4 * q4] * f_mine, acc[db][4 * q4 + 1] * f_mine,
+                                                          acc[db][4 * q4 + 2] * f_mine, acc[db][4 * q4 + 3] * f_mine};
     }
     lds_barrier();
-    __shared__ int sLast;
-    const long long unit = ((long long)b * p.heads_kv + g) * p.m_groups + mg;
-    const long long pidx0 = unit * p.splits;
-    auto tail = [&](auto half_tag) __attribute__((always_inline)) {
-        constexpr int db0 = decltype(half_tag)::value * HB;
-        // o[i]: channels 32*(db0 + i/4) + 8*(i%4) + 4*lh .. +3 of row my_row.
-        f32x4_t o[4 * HB];
+    if (w == 1 || !row_valid) return;
 #pragma unroll
-        for (int i = 0; i < 4 * HB; ++i) {
-            const int db = db0 + i / 4, q4 = i % 4;
-            const f32x4_t x = xbuf[(db * 4 + q4) * 64 + lane];
-            o[i] = f32x4_t{acc[db][4 * q4] * f_mine + x[0], acc[db][4 * q4 + 1] * f_mine + x[1],
-                           acc[db][4 * q4 + 2] * f_mine + x[2], acc[db][4 * q4 + 3] * f_mine + x[3]};
-        }
-        auto write_out = [&](const f32x4_t (&v)[4 * HB], float Mr, float Lr) __attribute__((always_inline)) {
-            if (!row_valid) return;
-            const float inv = (Lr > 0.0f) ? 1.0f / Lr : 0.0f;
-            uint16_t* O =
-                static_cast<uint16_t*>(p.o) + ((long long)(q_start + my_tok) * p.heads_q + my_head) * D + 4 * lh;
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-            for (int i = 0; i < 4 * HB; ++i)
-                store_u32x2(O + 32 * (db0 + i / 4) + 8 * (i % 4),
-                            u32x2_t{pack_bf16x2(v[i][0] * inv, v[i][1] * inv), pack_bf16x2(v[i][2] * inv, v[i][3] * inv)});
-            if (p.lse && db0 == 0 && lh == 0)
-                p.lse[(long long)my_head * p.total_q + q_start + my_tok] =
-                    (Lr > 0.0f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
-        };
-        if (p.splits == 1) {
-            write_out(o, M, L);
-            return;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4_t o = xbuf[(db * 4 + q4) * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] = acc[db][4 * q4 + e] * f_mine + o[e];
         }
 
-        // Several splits: write this split's partial; the last work group of
-        // the (sequence, kv head, row group) to arrive merges all of them.
-        if (row_valid) {
-            float* pacc = p.part_acc + ((pidx0 + sp) * ROWS + lr) * D + 4 * lh;
+    // Lane lr holds row my_row, channels 32*db + 8*q4 + 4*lh .. +3.
+    if (p.splits == 1) {
+        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+        uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + my_tok) * p.heads_q + my_head) * D + 4 * lh;
 #pragma unroll
-            for (int i = 0; i < 4 * HB; ++i)
-                *reinterpret_cast<f32x4_t*>(pacc + 32 * (db0 + i / 4) + 8 * (i % 4)) = o[i];
-            if (db0 == 0 && lh == 0) {
-                float* pml = p.part_ml + (pidx0 + sp) * 2 * ROWS;
-                pml[lr] = M;
-                pml[ROWS + lr] = L;
-            }
-        }
-        // Release the partial, then arrive. The counter holds (epoch << 32) |
-        // arrivals: a value tagged with another epoch (an earlier call, or
-        // memory never used as a counter) counts as no arrival. The last
-        // arrival resets it to 0, so a replay of the same call with the same
-        // epoch also starts from no arrival.
-        __threadfence();
-        lds_barrier();
-        if (tid == 0) {
-            unsigned long long* ctr = p.counters + unit;
-            unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            unsigned int seen;
-            while (true) {
-                seen = ((unsigned int)(old >> 32) == p.epoch) ? (unsigned int)old : 0u;
-                const unsigned long long want = ((unsigned long long)p.epoch << 32) | (seen + 1u);
-                if (__hip_atomic_compare_exchange_strong(ctr, &old, want, __ATOMIC_ACQ_REL, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT))
-                    break;
-            }
-            sLast = (seen + 1u == (unsigned int)p.splits) ? 1 : 0;
-        }
-        lds_barrier();
-        if (!sLast) return;
-        __threadfence();  // acquire: the other splits' partials are visible from here on
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+                store_u32x2(O + 32 * db + 8 * q4,
+                            u32x2_t{pack_bf16x2(acc[db][4 * q4] * inv, acc[db][4 * q4 + 1] * inv),
+                                    pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv)});
+        if (p.lse && lh == 0)
+            p.lse[(long long)my_head * p.total_q + q_start + my_tok] =
+                (L > 0.0f) ? (M + fast_log2(L)) * kLn2 : -INFINITY;
+        return;
+    }
+    const long long pidx = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits + sp;
+    float* pacc = p.part_acc + (pidx * ROWS + lr) * D + 4 * lh;
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4_t*>(pacc + 32 * db + 8 * q4) =
+                f32x4_t{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+    if (lh == 0) {
+        float* pml = p.part_ml + pidx * 2 * ROWS;
+        pml[lr] = M;
+        pml[ROWS + lr] = L;
+    }
+}
 
-        // Merge in split order (the same arithmetic whichever group is last):
-        // chunks of CH splits, all loads of a chunk in flight together, a
-        // running max across chunks.
-        constexpr int CH = 2;
-        float Mall = -INFINITY, Lall = 0.0f;
-        f32x4_t oa[4 * HB];
+// Merge the splits of one (sequence, kv head, row group): M = max_s m_s,
+// w_s = exp2(m_s - M), O = sum_s w_s acc_s / sum_s w_s l_s,
+// LSE = ln2 * (M + log2 sum_s w_s l_s). One thread per (row, 4 channels).
+// The splits are read in chunks of 8 whose loads are all issued before any
+// is used (one memory round trip per chunk), merged with a running max.
+constexpr int kCombineThreads = 64;  // small groups spread the few valid rows over many CUs
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void decode_gqa_combine_kernel(const GqaDecodeParams p) {
+    constexpr int TPR = D / 4;                     // threads per row
+    constexpr int RPB = kCombineThreads / TPR;     // rows per work group
+    constexpr int CH = 8;             // splits per chunk
+    int id = blockIdx.x;
+    const int rgrp = id % (ROWS / RPB);
+    id /= ROWS / RPB;
+    const int mg = id % p.m_groups;
+    id /= p.m_groups;
+    const int g = id % p.heads_kv;
+    const int b = id / p.heads_kv;
+    const int G = p.group;
+    const int q_start = p.cu_q[b];
+    const int sq = p.cu_q[b + 1] - q_start;
+    const int row = rgrp * RPB + (int)threadIdx.x / TPR;
+    const int r = mg * ROWS + row;
+    if (r >= sq * G) return;
+    const int d0 = ((int)threadIdx.x % TPR) * 4;
+    const int tok = r / G;
+    const int h = g * G + r % G;
+    const long long pidx0 = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits;
+    float M = -INFINITY, L = 0.0f;
+    f32x4_t o = f32x4_t{};
+    for (int s0 = 0; s0 < p.splits; s0 += CH) {
+        float ms[CH], ls[CH];
+        f32x4_t as[CH];
 #pragma unroll
-        for (int i = 0; i < 4 * HB; ++i) oa[i] = f32x4_t{};
-        for (int s0 = 0; s0 < p.splits; s0 += CH) {
-            float ms[CH], ls[CH];
-            f32x4_t as[CH][4 * HB];
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const bool in = s0 + j < p.splits;
-                const long long pi = pidx0 + (in ? s0 + j : 0);
-                ms[j] = in ? p.part_ml[pi * 2 * ROWS + lr] : -INFINITY;
-                ls[j] = p.part_ml[pi * 2 * ROWS + ROWS + lr];
-                const float* pa = p.part_acc + (pi * ROWS + lr) * D + 4 * lh;
-#pragma unroll
-                for (int i = 0; i < 4 * HB; ++i)
-                    as[j][i] = *reinterpret_cast<const f32x4_t*>(pa + 32 * (db0 + i / 4) + 8 * (i % 4));
-            }
-            float mc = Mall;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ms[j]);
-            if (mc == -INFINITY) continue;
-            const float a = fast_exp2(Mall - mc);
-            Lall *= a;
-#pragma unroll
-            for (int i = 0; i < 4 * HB; ++i) oa[i] *= a;
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const float ws = fast_exp2(ms[j] - mc);
-                Lall += ws * ls[j];
-#pragma unroll
-                for (int i = 0; i < 4 * HB; ++i) oa[i] += ws * as[j][i];
-            }
-            Mall = mc;
+        for (int j = 0; j < CH; ++j) {
+            const bool in = s0 + j < p.splits;
+            const long long pi = pidx0 + (in ? s0 + j : 0);
+            ms[j] = in ? p.part_ml[pi * 2 * ROWS + row] : -INFINITY;
+            ls[j] = p.part_ml[pi * 2 * ROWS + ROWS + row];
+            as[j] = *reinterpret_cast<const f32x4_t*>(p.part_acc + (pi * ROWS + row) * D + d0);
         }
-        write_out(oa, Mall, Lall);
-        if (tid == 0) __hip_atomic_store(p.counters + unit, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    if (w == 0)
-        tail(std::integral_constant<int, 0>{});
-    else
-        tail(std::integral_constant<int, 1>{});
+        float mc = M;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ms[j]);
+        if (mc == -INFINITY) continue;  // nothing visible so far
+        const float a = fast_exp2(M - mc);  // 0 while M is -inf
+        L *= a;
+        o *= a;
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            const float ws = fast_exp2(ms[j] - mc);  // 0 for splits past the end or with no keys
+            L += ws * ls[j];
+            o += ws * as[j];
+        }
+        M = mc;
+    }
+    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * D + d0;
+    store_u32x2(O, u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)});
+    if (p.lse && d0 == 0)
+        p.lse[(long long)h * p.total_q + q_start + tok] = (L > 0.0f) ? (M + fast_log2(L)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -436,11 +418,17 @@ hipError_t launch_gqa(const GqaDecodeParams& p, hipStream_t stream) {
     const long long units = (long long)p.batch * p.heads_kv * p.m_groups;
     if (units <= 0) return hipSuccess;
     const long long grid_split = units * p.splits;
-    if (grid_split > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    constexpr int RPB = kCombineThreads / (D / 4);
+    const long long grid_comb = units * (ROWS / RPB);
+    if (grid_split > 0x7fffffffLL || grid_comb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)
         hipLaunchKernelGGL((decode_gqa_split_kernel<D, true>), dim3((unsigned)grid_split), dim3(NT), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_gqa_split_kernel<D, false>), dim3((unsigned)grid_split), dim3(NT), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.splits == 1) return e;
+    hipLaunchKernelGGL((decode_gqa_combine_kernel<D>), dim3((unsigned)grid_comb), dim3(kCombineThreads), 0, stream,
+                       p);
     return hipGetLastError();
 }
 

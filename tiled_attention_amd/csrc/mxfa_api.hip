@@ -9,7 +9,6 @@
 #include <stdint.h>
 #include <stdio.h>
 
-#include <atomic>
 #include <mutex>
 
 #include "mxfa.h"
@@ -153,25 +152,12 @@ int plan_gqa_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, 
     return (int)s;
 }
 
-// Workspace of the standard-head decode: the split partials, then one 8-byte
-// arrival counter per (sequence, kv head, row group).
 size_t gqa_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, int head_dim, int splits) {
     if (splits <= 1) return 0;
     const int group = heads_q / heads_kv;
     const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kGqaRows - 1) / mxfa::kGqaRows;
-    const long long units = (long long)batch * heads_kv * m_groups;
-    const long long parts = units * splits;
-    return (size_t)parts * (size_t)mxfa::kGqaRows * ((size_t)head_dim + 2) * sizeof(float) +
-           (size_t)units * sizeof(unsigned long long);
-}
-
-// Tag of one standard-head decode call for its arrival counters: never 0, and
-// different from the previous 2^32 - 1 calls in this process.
-unsigned int next_epoch() {
-    static std::atomic<unsigned int> counter{0};
-    unsigned int e = ++counter;
-    while (e == 0) e = ++counter;
-    return e;
+    const long long parts = (long long)batch * heads_kv * m_groups * splits;
+    return (size_t)parts * (size_t)mxfa::kGqaRows * ((size_t)head_dim + 2) * sizeof(float);
 }
 
 // Checks and launch shared by the contiguous (cu_k) and paged (pg) decode
@@ -518,8 +504,6 @@ mxfa_status mxfa_decode_splitkv_gqa(const void* q, const void* k, const void* v,
         const long long parts = (long long)batch * heads_kv * p.m_groups * splits;
         p.part_acc = static_cast<float*>(workspace);
         p.part_ml = p.part_acc + parts * mxfa::kGqaRows * head_dim;
-        p.counters = reinterpret_cast<unsigned long long*>(p.part_ml + parts * 2 * mxfa::kGqaRows);
-        p.epoch = next_epoch();
     }
     p.causal = causal ? 1 : 0;
     p.window_left = window_left;

@@ -86,8 +86,6 @@ struct GqaDecodeParams {
     const int32_t* cu_k;
     float* part_acc;         // [batch, heads_kv, m_groups, splits, 32, head_dim] fp32 (splits > 1)
     float* part_ml;          // [batch, heads_kv, m_groups, splits, 2, 32] fp32 (max, sum)
-    unsigned long long* counters;  // [batch, heads_kv, m_groups] arrivals, tagged with the epoch
-    unsigned int epoch;      // this call's tag (never 0)
     int batch;
     int total_q;
     int heads_q;
