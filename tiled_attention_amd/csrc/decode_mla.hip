@@ -571,8 +571,9 @@ void decode_split_kernel(const DecodeParams p) {
 }
 
 // Merge the splits: M = max_s m_s, w_s = exp2(m_s - M),
-// O = sum_s w_s acc_s / sum_s w_s l_s, LSE = ln2 * (M + log2 sum_s w_s l_s).
-// One thread per (row, 16 channels); 8 rows per work group.
+// O = sum_s w_s acc_s / sum_s w_s l_s, LSE = ln2 * (M + log2 sum_s w_s l_s),
+// with a running max over chunks of splits. One thread per (row, 16
+// channels); 8 rows per work group.
 constexpr int CROWS = NTHREADS / 32;
 
 __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodeParams p) {
@@ -593,27 +594,47 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
     const int tok = r / G;
     const int h = g * G + r % G;
     const long long pidx0 = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits;
-    float M = -INFINITY;
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.part_ml[(pidx0 + s) * 2 * ROWS + row]);
-    float L = 0.0f;
+    // One pass with a running max over chunks of CH splits; all loads of a
+    // chunk are issued before any is used (one memory round trip per chunk).
+    constexpr int CH = 2;
+    float M = -INFINITY, L = 0.0f;
     float o[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[j] = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < p.splits; ++s) {
-            const float* pml = p.part_ml + (pidx0 + s) * 2 * ROWS;
-            const float ws = fast_exp2(pml[row] - M);
-            L += ws * pml[ROWS + row];
-            const f32x4_t* a = reinterpret_cast<const f32x4_t*>(p.part_acc + ((pidx0 + s) * ROWS + row) * DV + d0);
+    for (int s0 = 0; s0 < p.splits; s0 += CH) {
+        float ms[CH], ls[CH];
+        f32x4_t as[CH][4];
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const bool in = s0 + c < p.splits;
+            const long long pi = pidx0 + (in ? s0 + c : 0);
+            ms[c] = in ? p.part_ml[pi * 2 * ROWS + row] : -INFINITY;
+            ls[c] = p.part_ml[pi * 2 * ROWS + ROWS + row];
+            const f32x4_t* a = reinterpret_cast<const f32x4_t*>(p.part_acc + (pi * ROWS + row) * DV + d0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) as[c][j] = a[j];
+        }
+        float mc = M;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) mc = fmaxf(mc, ms[c]);
+        if (mc == -INFINITY) continue;  // nothing visible so far
+        const float rs = fast_exp2(M - mc);  // 0 while M is -inf
+        L *= rs;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j] *= rs;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const float ws = fast_exp2(ms[c] - mc);  // 0 for splits past the end or with no keys
+            L += ws * ls[c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4_t v = a[j];
-                o[4 * j + 0] += ws * v[0];
-                o[4 * j + 1] += ws * v[1];
-                o[4 * j + 2] += ws * v[2];
-                o[4 * j + 3] += ws * v[3];
+                o[4 * j + 0] += ws * as[c][j][0];
+                o[4 * j + 1] += ws * as[c][j][1];
+                o[4 * j + 2] += ws * as[c][j][2];
+                o[4 * j + 3] += ws * as[c][j][3];
             }
         }
+        M = mc;
     }
     const float inv = (L > 0.0f) ? p.v_scale / L : 0.0f;  // v_scale: the fp8 cache's dequantisation scale
     uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * DV + d0;
