@@ -144,6 +144,14 @@ void fwd_bf16_kernel(const FwdParams p) {
     const int qi = wrow0 + lr;
     const bool q_valid = qi < sq;
     const KeyRange mine = visible_range(qi + off, sk, p.causal, p.window_left, p.window_right);
+    // The row's keys as lo + [0, span] (an empty range becomes one no key
+    // reaches), for the masked tiles: key kt + 4*lh + c (c a constant of the
+    // register) is visible iff (unsigned)(c - (lo - kt - 4*lh)) <= span.
+    int m_lo = mine.lo, m_span = mine.hi - mine.lo;
+    if (m_span < 0) {
+        m_lo = 0x40000000;
+        m_span = 0;
+    }
 
     // Q^T as the B operand: lane holds row qi, contraction chunk ks*16 + lh*8.
     bf16x8_t qreg[KSTEPS];
@@ -233,7 +241,11 @@ void fwd_bf16_kernel(const FwdParams p) {
     };
     // Logits (raw scores in mode 0), mask, and the tile's row max in log2 units.
     auto logits_max = [&](auto masked_tag, f32x16_t (&s)[2], int kt) -> float {
-        constexpr bool kMasked = decltype(masked_tag)::value;
+        // 0: every key visible; 1: keys below the tile are all visible, test
+        // the upper bound only; 2: test both bounds.
+        constexpr int kMask = decltype(masked_tag)::value;
+        const int hiT = mine.hi - kt - 4 * lh;
+        const int loT = m_lo - kt - 4 * lh;
         float m = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -242,10 +254,9 @@ void fwd_bf16_kernel(const FwdParams p) {
                 float x = s[kb][r];
                 if constexpr (kMode == 1) x = x * p.x_mul;
                 if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
-                if constexpr (kMasked) {
-                    const int key = kt + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    x = (key >= mine.lo && key <= mine.hi) ? x : -INFINITY;
-                }
+                const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+                if constexpr (kMask == 1) x = (c <= hiT) ? x : -INFINITY;
+                if constexpr (kMask == 2) x = ((unsigned)(c - loT) <= (unsigned)m_span) ? x : -INFINITY;
                 s[kb][r] = x;
                 m = fmaxf(m, x);
             }
@@ -254,6 +265,10 @@ void fwd_bf16_kernel(const FwdParams p) {
         if constexpr (kMode == 0) m *= c_exp;
         return m;
     };
+    // Every row of this wave sees all keys below kt (its lower bounds are
+    // non-decreasing in the row, so the last row's decides), and no row's
+    // range is empty.
+    auto lows_visible = [&](int kt) { return wave_rows_valid && wlast.lo <= kt && wfirst.lo <= wfirst.hi; };
     auto tile_full = [&](int kt) {
         const int t_last = kt + BN - 1;
         return wave_rows_valid && t_last < sk && kt >= wlast.lo && t_last <= wfirst.hi;
@@ -351,7 +366,9 @@ void fwd_bf16_kernel(const FwdParams p) {
     // transposing V reads run AHEAD MFMAs ahead.
     auto pv_max = [&](auto masked_tag, const uint32_t (&pk)[2][8], const char* vt_lds, f32x16_t (&sn)[2], int kt,
                       auto&& mid_hook) __attribute__((always_inline)) -> float {
-        constexpr bool kMasked = decltype(masked_tag)::value;
+        constexpr int kMask = decltype(masked_tag)::value;  // as for logits_max
+        const int hiT = mine.hi - kt - 4 * lh;
+        const int loT = m_lo - kt - 4 * lh;
         constexpr int NP = 4 * DBLK;  // MFMAs: n = DBLK*step + db, step = 2*kb + half (16 keys each)
         constexpr int EPS = 32 / NP;  // score elements per slice
         constexpr int AHEAD = 4;
@@ -391,10 +408,9 @@ void fwd_bf16_kernel(const FwdParams p) {
                 float x = sn[skb][r];
                 if constexpr (kMode == 1) x = x * p.x_mul;
                 if constexpr (kMode == 2) x = score_to_logit<true>(x, p.x_mul, p.cap_mul, p.cap_out);
-                if constexpr (kMasked) {
-                    const int key = kt + skb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                    x = (key >= mine.lo && key <= mine.hi) ? x : -INFINITY;
-                }
+                const int c = skb * 32 + 8 * (r >> 2) + (r & 3);
+                if constexpr (kMask == 1) x = (c <= hiT) ? x : -INFINITY;
+                if constexpr (kMask == 2) x = ((unsigned)(c - loT) <= (unsigned)m_span) ? x : -INFINITY;
                 sn[skb][r] = x;
                 mm = fmaxf(mm, x);
             }
@@ -419,7 +435,12 @@ void fwd_bf16_kernel(const FwdParams p) {
         f32x16_t sa[2], sb[2];
         float mt_a = -INFINITY, mt_b = -INFINITY;
         qk(sa, sK0, [] {});
-        mt_a = tile_full(kt0) ? logits_max(std::false_type{}, sa, kt0) : logits_max(std::true_type{}, sa, kt0);
+        using mask0 = std::integral_constant<int, 0>;
+        using mask1 = std::integral_constant<int, 1>;
+        using mask2 = std::integral_constant<int, 2>;
+        mt_a = tile_full(kt0)      ? logits_max(mask0{}, sa, kt0)
+               : lows_visible(kt0) ? logits_max(mask1{}, sa, kt0)
+                                   : logits_max(mask2{}, sa, kt0);
         // The first step reads K1 and V0. Each of them is loaded by all four
         // waves, and a wave's own wait covers only its own part: wait for all
         // of this wave's loads, then the barrier covers the other waves'
@@ -458,9 +479,11 @@ void fwd_bf16_kernel(const FwdParams p) {
                 if (v_more) issue_part(Vseg, kt + BN, v_fill, 0, H);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
                 if (tile_full(kt + BN))
-                    mt_next = pv_max(std::false_type{}, pk, v_use, s_next, kt + BN, v_second);
+                    mt_next = pv_max(mask0{}, pk, v_use, s_next, kt + BN, v_second);
+                else if (lows_visible(kt + BN))
+                    mt_next = pv_max(mask1{}, pk, v_use, s_next, kt + BN, v_second);
                 else
-                    mt_next = pv_max(std::true_type{}, pk, v_use, s_next, kt + BN, v_second);
+                    mt_next = pv_max(mask2{}, pk, v_use, s_next, kt + BN, v_second);
             } else {
                 k_second();
                 exp_tile(s_cur, pk);
