@@ -19,14 +19,16 @@
 // O^T = V^T P^T (the accumulator layout of S^T is the operand layout of
 // P^T); the V^T operand comes from LDS through ds_read_b64_tr_b16. O^T keeps
 // one query per lane, so the online-softmax rescale is one multiplier per
-// lane, and it is skipped unless some row's max grew by more than 2^8.
+// lane. P of a tile is computed against the running max of the earlier
+// tiles; only when some lane's sum of it exceeds 2^8 (the max grew) is the
+// tile's row max taken, the accumulator rescaled and P recomputed.
 //
 // Software pipeline inside each wave (two S register sets): while the MFMAs
 // compute S for tile j+1, the vector ALU turns S of tile j into P; while the
-// MFMAs accumulate P V for tile j, the vector ALU masks tile j+1 and takes
-// its row max. K therefore runs one tile ahead of V: K tiles j+1 (in use) and
-// j+2 (arriving), V tiles j (in use) and j+1 (arriving) share two buffers
-// each, filled by buffer loads that write LDS directly (out-of-range keys
+// MFMAs accumulate P V for tile j, the vector ALU masks tile j+1 (and applies
+// the scale or the cap in those modes). K therefore runs one tile ahead of V:
+// K tiles j+1 (in use) and j+2 (arriving), V tiles j (in use) and j+1
+// (arriving) share two buffers each, filled by buffer loads that write LDS directly (out-of-range keys
 // read as zero). The 16-byte chunks of a row are XOR-swizzled so that the K
 // operand reads (16 rows x one chunk) and the transposing V reads (4 rows x 4
 // chunks per half wave) hit distinct banks. Fully visible tiles take a branch
@@ -42,6 +44,7 @@ constexpr int BM = 128;        // query rows per work group
 constexpr int BN = 64;         // keys per tile
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float kLazyRescale = 8.0f;  // log2 units: rescale when a row max grows by > 2^8
+constexpr float kOptimisticSum = 256.0f;  // a tile's P sum (per lane) up to which no p can exceed 2^8
 
 // Chunk swizzle of an LDS row (16-byte chunks): physical = logical ^ swz(row).
 template <int D>
@@ -300,6 +303,30 @@ void fwd_bf16_kernel(const FwdParams p) {
                 pk[kb][r >> 1] = pack_bf16x2(p0, p1);
             }
         }
+        return psum;
+    };
+    // Optimistic max: P of a tile is first computed against the running max
+    // of the earlier tiles. If every lane's sum of it stays <= 2^8, every p
+    // is <= 2^8 -- the bound the lazy rescale keeps -- and the tile is done
+    // without its row max. Otherwise (the max grew, or no key was seen yet)
+    // take the tile's max, rescale and recompute P.
+    auto settle = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8], float psum) __attribute__((always_inline)) {
+        if (wave_any(m_run == -INFINITY || psum > kOptimisticSum)) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            if constexpr (kMode == 0) mt *= c_exp;
+            const float m_new = fmaxf(m_run, mt);
+            const float alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_part *= alpha;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+            psum = exp_tile(s, pk);
+        }
         l_part += psum;
     };
     // O^T += V^T P^T for one tile.
@@ -359,13 +386,13 @@ void fwd_bf16_kernel(const FwdParams p) {
             if (m == NM / 2 - 1) mid_hook();
             __builtin_amdgcn_sched_barrier(0);
         }
-        l_part += psum;
+        return psum;
     };
     // Phase B, fused: O += V_j P_j on the MFMAs while the vector ALU takes
-    // the logits, mask and row max of S_{j+1}, a slice after each MFMA; the
+    // the logits and the mask of S_{j+1}, a slice after each MFMA; the
     // transposing V reads run AHEAD MFMAs ahead.
-    auto pv_max = [&](auto masked_tag, const uint32_t (&pk)[2][8], const char* vt_lds, f32x16_t (&sn)[2], int kt,
-                      auto&& mid_hook) __attribute__((always_inline)) -> float {
+    auto pv_mask = [&](auto masked_tag, const uint32_t (&pk)[2][8], const char* vt_lds, f32x16_t (&sn)[2], int kt,
+                      auto&& mid_hook) __attribute__((always_inline)) {
         constexpr int kMask = decltype(masked_tag)::value;  // as for logits_max
         const int hiT = mine.hi - kt - 4 * lh;
         const int loT = m_lo - kt - 4 * lh;
@@ -385,7 +412,6 @@ void fwd_bf16_kernel(const FwdParams p) {
             r0[n] = rd(n, 0);
             r1[n] = rd(n, 1);
         }
-        float mm = -INFINITY;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int n = 0; n < NP; ++n) {
@@ -412,14 +438,10 @@ void fwd_bf16_kernel(const FwdParams p) {
                 if constexpr (kMask == 1) x = (c <= hiT) ? x : -INFINITY;
                 if constexpr (kMask == 2) x = ((unsigned)(c - loT) <= (unsigned)m_span) ? x : -INFINITY;
                 sn[skb][r] = x;
-                mm = fmaxf(mm, x);
             }
             if (n == NP / 2 - 1) mid_hook();
             __builtin_amdgcn_sched_barrier(0);
         }
-        mm = fmaxf(mm, __shfl_xor(mm, 32));
-        if constexpr (kMode == 0) mm *= c_exp;
-        return mm;
     };
 
     if (kv_lo <= kv_hi) {
@@ -433,7 +455,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"i"(2 * LOADS) : "memory");
         lds_barrier();
         f32x16_t sa[2], sb[2];
-        float mt_a = -INFINITY, mt_b = -INFINITY;
+        float mt_a = -INFINITY;
         qk(sa, sK0, [] {});
         using mask0 = std::integral_constant<int, 0>;
         using mask1 = std::integral_constant<int, 1>;
@@ -441,6 +463,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         mt_a = tile_full(kt0)      ? logits_max(mask0{}, sa, kt0)
                : lows_visible(kt0) ? logits_max(mask1{}, sa, kt0)
                                    : logits_max(mask2{}, sa, kt0);
+        update_max(mt_a);  // later tiles start from this max (optimistic)
         // The first step reads K1 and V0. Each of them is loaded by all four
         // waves, and a wave's own wait covers only its own part: wait for all
         // of this wave's loads, then the barrier covers the other waves'
@@ -448,11 +471,10 @@ void fwd_bf16_kernel(const FwdParams p) {
         wait_vmem();
         lds_barrier();
 
-        // Tile j (parity P = j % 2): S_j in s_cur (masked, max mt_cur); K(j+1)
+        // Tile j (parity P = j % 2): S_j in s_cur (masked); K(j+1)
         // in sK[1-P] and V(j) in sV[P] are resident; K(j+2) goes to sK[P] and
         // V(j+1) to sV[1-P].
-        auto step = [&](auto has_next_tag, auto parity_tag, int j, f32x16_t (&s_cur)[2], float mt_cur,
-                        f32x16_t (&s_next)[2], float& mt_next) {
+        auto step = [&](auto has_next_tag, auto parity_tag, int j, f32x16_t (&s_cur)[2], f32x16_t (&s_next)[2]) {
             constexpr bool kNext = decltype(has_next_tag)::value;
             constexpr int P = decltype(parity_tag)::value;
             char* const k_fill = P ? sK1 : sK0;
@@ -471,22 +493,21 @@ void fwd_bf16_kernel(const FwdParams p) {
                 if (v_more) issue_part(Vseg, kt + BN, v_fill, H, LOADS);
             };
             if (k_more) issue_part(Kseg, kt + 2 * BN, k_fill, 0, H);
-            update_max(mt_cur);
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
-                qk_exp(s_next, k_use, s_cur, pk, k_second);
+                settle(s_cur, pk, qk_exp(s_next, k_use, s_cur, pk, k_second));
                 if (v_more) issue_part(Vseg, kt + BN, v_fill, 0, H);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
                 if (tile_full(kt + BN))
-                    mt_next = pv_max(mask0{}, pk, v_use, s_next, kt + BN, v_second);
+                    pv_mask(mask0{}, pk, v_use, s_next, kt + BN, v_second);
                 else if (lows_visible(kt + BN))
-                    mt_next = pv_max(mask1{}, pk, v_use, s_next, kt + BN, v_second);
+                    pv_mask(mask1{}, pk, v_use, s_next, kt + BN, v_second);
                 else
-                    mt_next = pv_max(mask2{}, pk, v_use, s_next, kt + BN, v_second);
+                    pv_mask(mask2{}, pk, v_use, s_next, kt + BN, v_second);
             } else {
                 k_second();
-                exp_tile(s_cur, pk);
+                settle(s_cur, pk, exp_tile(s_cur, pk));
                 if (v_more) issue_part(Vseg, kt + BN, v_fill, 0, H);
                 pv(pk, v_use, v_second);
             }
@@ -498,14 +519,14 @@ void fwd_bf16_kernel(const FwdParams p) {
 
         int j = 0;
         for (; j + 2 < ntiles; j += 2) {
-            step(std::true_type{}, even{}, j, sa, mt_a, sb, mt_b);
-            step(std::true_type{}, odd{}, j + 1, sb, mt_b, sa, mt_a);
+            step(std::true_type{}, even{}, j, sa, sb);
+            step(std::true_type{}, odd{}, j + 1, sb, sa);
         }
         if (j + 1 < ntiles) {
-            step(std::true_type{}, even{}, j, sa, mt_a, sb, mt_b);
-            step(std::false_type{}, odd{}, j + 1, sb, mt_b, sa, mt_a);
+            step(std::true_type{}, even{}, j, sa, sb);
+            step(std::false_type{}, odd{}, j + 1, sb, sa);
         } else {
-            step(std::false_type{}, even{}, j, sa, mt_a, sb, mt_b);
+            step(std::false_type{}, even{}, j, sa, sb);
         }
     }
 
