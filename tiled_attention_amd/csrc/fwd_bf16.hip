@@ -28,11 +28,11 @@
 // MFMAs accumulate P V for tile j, the vector ALU masks tile j+1 (and applies
 // the scale or the cap in those modes). K therefore runs one tile ahead of V:
 // K tiles j+1 (in use) and j+2 (arriving), V tiles j (in use) and j+1
-// (arriving) share two buffers each, filled by buffer loads that write LDS directly (out-of-range keys
-// read as zero). The 16-byte chunks of a row are XOR-swizzled so that the K
-// operand reads (16 rows x one chunk) and the transposing V reads (4 rows x 4
-// chunks per half wave) hit distinct banks. Fully visible tiles take a branch
-// without per-element mask tests.
+// (arriving) share two buffers each, filled by buffer loads that write LDS
+// directly (out-of-range keys read as zero). The 16-byte chunks of a row are
+// XOR-swizzled so that the K operand reads (16 rows x one chunk) and the
+// transposing V reads (4 rows x 4 chunks per half wave) hit distinct banks.
+// Fully visible tiles take a branch without per-element mask tests.
 #include <type_traits>
 
 #include "mxfa_device.h"
