@@ -20,7 +20,9 @@
 //       18 v_mfma_f32_32x32x16_bf16 (its Q^T slice lives in accumulation
 //       registers); the two waves of a row block swap partials through LDS
 //       and both add them (same operands, same order: the same S^T);
-//   softmax: mask, row max (one lane exchange), lazy rescale, exp2, done
+//   softmax: logits and mask, then exp2 against the running max of the
+//       earlier tiles; only when some lane's sum of P exceeds 2^8 is the
+//       tile's row max taken (one lane exchange) and P recomputed; done
 //       identically by both waves of the row block;
 //   PV: O^T (channels 256*ch..+255 x 32 rows) += V^T P^T with 16 MFMAs;
 //       P^T is the S^T accumulator re-packed to bf16 in place and the V^T
@@ -47,7 +49,6 @@ constexpr int ROWB = DQK * 2;            // 1152 bytes per latent row
 constexpr int CPR = DQK / 8;             // 72 chunks of 16 bytes per row
 constexpr int TILEB = BN * ROWB;         // 36864 bytes per tile
 constexpr int LOADS = TILEB / (16 * NTHREADS);  // 9 loads per thread per tile
-constexpr float kLazyRescale = 8.0f;
 static_assert(LOADS * 16 * NTHREADS == TILEB, "tile must split into whole loads");
 
 // Chunk swizzle of a 1152-byte row (physical chunk = logical ^ swz(row)).
@@ -333,7 +334,10 @@ void decode_split_kernel(const DecodeParams p) {
             kr[ks] = __builtin_bit_cast(bf16x8_t, lds_read16(tile + kxl[ks & 3] + 128 * (ks >> 2)));
         f32x16_t sn = f32x16_t{};
         f32x16_t x = s_cur;
-        float mt = -INFINITY, mt_pair = -INFINITY, nb = 0.0f, psum = 0.0f;
+        // Optimistic max: P against the running max of the earlier tiles;
+        // the tile's own max only when some lane's sum of P exceeds 2^8.
+        const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
+        float psum = 0.0f;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -341,7 +345,7 @@ void decode_split_kernel(const DecodeParams p) {
                 kr[ks + AHEAD] = __builtin_bit_cast(
                     bf16x8_t, lds_read16(tile + kxl[(ks + AHEAD) & 3] + 128 * ((ks + AHEAD) >> 2)));
             sn = mfma32x32x16(kr[ks], qreg[ks], sn);
-            if (ks >= 2 && ks < 10) {  // logits, mask and max of elements 2(ks-2), 2(ks-2)+1
+            if (ks >= 2 && ks < 10) {  // logits and mask of elements 2(ks-2), 2(ks-2)+1
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const int r = 2 * (ks - 2) + e;
@@ -350,33 +354,36 @@ void decode_split_kernel(const DecodeParams p) {
                     const int key = kt + 8 * (r >> 2) + 4 * lh + (r & 3);
                     v = ((unsigned)(key - key_lo) <= (unsigned)key_span) ? v : -INFINITY;
                     x[r] = v;
-                    mt = fmaxf(mt, v);
                 }
             }
-            if (ks == 10) mt_pair = __shfl_xor(mt, 32);
+            if (ks >= 10) {  // exp2 and packing of elements 2(ks-10), 2(ks-10)+1
+                const int r = 2 * (ks - 10);
+                const float p0 = fast_exp2(x[r] + nb);
+                const float p1 = fast_exp2(x[r + 1] + nb);
+                psum += p0 + p1;
+                pk[r >> 1] = pack_bf16x2(p0, p1);
+            }
             if (ks == 6) mid_hook();
-            if (ks == 12) {
-                mt = fmaxf(mt, mt_pair);
-                const bool grow = mt > m_run + kLazyRescale;
-                const float m_new = grow ? mt : m_run;
-                alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
-                m_run = m_new;
-                nb = (m_run == -INFINITY) ? 0.0f : -m_run;
-            }
-            if (ks >= 13) {  // exp2 and packing, 4 or 3 elements per slice
-                constexpr int kFirst[5] = {0, 4, 6, 10, 12};
-                constexpr int kCount[5] = {4, 2, 4, 2, 4};
-                const int i0 = kFirst[ks - 13];
-#pragma unroll
-                for (int e = 0; e < kCount[ks - 13]; e += 2) {
-                    const int r = i0 + e;
-                    const float p0 = fast_exp2(x[r] + nb);
-                    const float p1 = fast_exp2(x[r + 1] + nb);
-                    psum += p0 + p1;
-                    pk[r >> 1] = pack_bf16x2(p0, p1);
-                }
-            }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        alpha = 1.0f;
+        if (wave_any(m_run == -INFINITY || psum > 256.0f)) {
+            float mt = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            const float m_new = fmaxf(m_run, mt);
+            alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            const float nb2 = (m_run == -INFINITY) ? 0.0f : -m_run;
+            psum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const float p0 = fast_exp2(x[r] + nb2);
+                const float p1 = fast_exp2(x[r + 1] + nb2);
+                psum += p0 + p1;
+                pk[r >> 1] = pack_bf16x2(p0, p1);
+            }
         }
         l_part = l_part * alpha + psum;
         return sn;
