@@ -499,6 +499,35 @@ def test_full_chunked_prefill_bf16():
     _full_dense_or_varlen("chunked_prefill_bf16", 384)
 
 
+def test_decode_long_context():
+    # 131072 keys per sequence (151 MB of latent rows each): large offsets and
+    # the automatic split plan at long range, checked on sampled rows.
+    lq, lk = [4, 1], [131072, 70001]
+    p = workloads.make_problem(3800, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    print("[decode] long context", flush=True)
+    scale = 1.0 / math.sqrt(576)
+    o_g, lse_g = _run_decode(p, 16, True, (-1, -1), 0.0, 0, scale)
+    rows = np.array([(t, h) for t in range(5) for h in (0, 5, 15)], dtype=np.int64)
+    import oracle
+
+    kv = to_np(p["kv"])
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kv, kv[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), causal=True, scale=scale, rows=rows)
+    compare(o_g[rows[:, 0], rows[:, 1]], lse_g.T[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "long context")
+
+
+def test_gqa_decode_long_context():
+    lq, lk = [1, 2], [65536, 40000]
+    p = workloads.make_problem(3810, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=lq, lens_k=lk)
+    print("[gqa-decode] long context", flush=True)
+    scale = 1.0 / math.sqrt(128)
+    o_g, lse_g = _run_gqa(p, True, (-1, -1), 0.0, 0, scale)
+    rows = np.array([(t, h) for t in range(3) for h in (0, 7, 8, 31)], dtype=np.int64)
+    o_ref, lse_ref, _ = oracle_varlen(p, causal=True, window=(-1, -1), softcap=0.0, scale=scale, rows=rows)
+    compare(o_g[rows[:, 0], rows[:, 1]], lse_g.T[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "long context")
+
+
 def test_prefill_after_kernels_that_leave_other_data_in_lds():
     # Regression: a tile is loaded into LDS by all waves of a work group, and a
     # wave's own wait covers only its part, so every read of a tile must come
