@@ -133,6 +133,68 @@ def test_zero_query_lse_counts_keys():
         assert abs(lse[0, 0, i].item() - math.log(cnt)) < 1e-4
 
 
+def _one_key_expectation(q, k, v, lens_q, lens_k, hq, hkv, scale):
+    """Window (0, 0): row i of a segment sees only key i + Sk - Sq (when that
+    key exists). Then P is a single weight, O is that key's V row and the LSE
+    is its scaled score (fp64 from the stored values); other rows see no key."""
+    qn, kn, vn = (t.double().numpy() for t in (q, k, v))  # exact widening of the stored values
+    g = hq // hkv
+    o = np.zeros((qn.shape[0], hq, vn.shape[2]))
+    lse = np.full((qn.shape[0], hq), -np.inf)
+    sq0 = sk0 = 0
+    for lq, lk in zip(lens_q, lens_k):
+        for i in range(lq):
+            pos = i + lk - lq
+            if 0 <= pos < lk:
+                for h in range(hq):
+                    o[sq0 + i, h] = vn[sk0 + pos, h // g]
+                    lse[sq0 + i, h] = scale * float(np.dot(qn[sq0 + i, h], kn[sk0 + pos, h // g]))
+        sq0 += lq
+        sk0 += lk
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_zero_returns_the_diagonal_value(dtype):
+    lens_q, lens_k = [5, 130, 0, 70, 40], [5, 200, 10, 300, 20]
+    p = workloads.make_problem(11, dtype=dtype, heads_q=4, heads_kv=2, d_qk=128, d_v=128, lens_q=lens_q,
+                               lens_k=lens_k)
+    scale = 128 ** -0.5
+    print(f"[closed form] window (0, 0) {dtype}", flush=True)
+    o_g, lse_g = gpu_varlen(p, causal=True, window=(0, 0), softcap=0.0, scale=scale)
+    o_x, lse_x = _one_key_expectation(p["q"], p["k"], p["v"], lens_q, lens_k, 4, 2, scale)
+    assert np.array_equal(np.isneginf(lse_g.T), np.isneginf(lse_x))
+    fin = np.isfinite(lse_x)
+    assert np.abs(lse_g.T[fin] - lse_x[fin]).max() <= 1e-4
+    if dtype == "bf16":
+        assert np.array_equal(o_g, o_x)  # a single weight of 1 rounds back to the stored value
+    else:
+        assert np.abs(o_g - o_x).max() <= 1e-5
+
+
+def test_window_zero_decodes_return_the_diagonal_value():
+    scale = 1.0 / math.sqrt(576)
+    lens_q, lens_k = [4, 1, 3], [300, 64, 700]
+    p = workloads.make_problem(12, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=lens_q,
+                               lens_k=lens_k, shared_kv=True)
+    print("[closed form] window (0, 0) latent decode", flush=True)
+    o_g, lse_g = _run_decode(p, 16, False, (0, 0), 0.0, 3, scale)
+    kv = p["kv"]
+    o_x, lse_x = _one_key_expectation(p["q"], kv, kv[:, :, :512].contiguous(), lens_q, lens_k, 16, 1, scale)
+    assert np.array_equal(o_g, o_x)
+    assert np.abs(lse_g.T - lse_x).max() <= 1e-4
+
+    scale = 128 ** -0.5
+    lens_q, lens_k = [1, 3, 2], [2000, 70, 129]
+    p = workloads.make_problem(13, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=lens_q,
+                               lens_k=lens_k)
+    print("[closed form] window (0, 0) standard-head decode", flush=True)
+    o_g, lse_g = _run_gqa(p, True, (0, 0), 0.0, 4, scale)
+    o_x, lse_x = _one_key_expectation(p["q"], p["k"], p["v"], lens_q, lens_k, 32, 4, scale)
+    assert np.array_equal(o_g, o_x)
+    assert np.abs(lse_g.T - lse_x).max() <= 1e-4
+
+
 def test_gqa_equals_mha_bitwise():
     p = workloads.make_problem(9, dtype="bf16", heads_q=8, heads_kv=2, d_qk=128, d_v=128, lens_q=[200] * 2,
                                lens_k=[200] * 2, dense=True)
