@@ -364,8 +364,9 @@ def main():
         pmc_summarize(args.pmc_summarize[0], args.pmc_summarize[1], args.copy_probe_mb)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
-              "(the multi-GPU sharding is a design, see DESIGN.md)", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; --gpus must be 1 "
+              "(sharding across GPUs by (sequence, kv head) groups is designed but not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -60,7 +60,7 @@ typedef struct ihipStream_t* mxfa_stream_t; /* the same handle as hipStream_t */
 typedef enum {
     MXFA_OK = 0,
     MXFA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent heads, ... */
-    MXFA_ERR_UNSUPPORTED = 2, /* head dim or dtype this build has no kernel for */
+    MXFA_ERR_UNSUPPORTED = 2, /* head dim or dtype the library has no kernel for */
     MXFA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query says */
     MXFA_ERR_HIP = 4          /* the HIP runtime reported an error (launch, device query) */
 } mxfa_status;
