@@ -1,0 +1,126 @@
+"""The boundary from C: include/mxfa.h compiles as C11 and C++17, and a plain
+C program (tests/c_abi/caller.c, HIP runtime C API only) links libmxfa.so.
+
+* CPU: the program runs the host-side argument checks and reads the version.
+* GPU: it runs the dense prefill and the latent decode on a stream of its own;
+  its outputs equal the Python binding's, bit for bit, on the same inputs.
+"""
+from __future__ import annotations
+
+import math
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import tiled_attention_amd as mx
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+SRC = os.path.join(ROOT, "tests", "c_abi", "caller.c")
+
+
+def _need_gcc():
+    if shutil.which("gcc") is None or not os.path.isdir(os.path.join(ROCM, "include", "hip")):
+        pytest.skip("gcc or the HIP headers are not available")
+
+
+def _library():
+    if not os.path.exists(mx.library_path()):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    return mx.library_path()
+
+
+def _build_caller(tmp_path):
+    _need_gcc()
+    libdir = os.path.dirname(_library())
+    exe = str(tmp_path / "caller")
+    subprocess.run(["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-I", os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__", SRC, "-o", exe, "-L", libdir,
+                    "-lmxfa", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", f"-Wl,-rpath,{libdir}",
+                    f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}"], check=True, capture_output=True, text=True)
+    return exe
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_compiles_alone(lang, tmp_path):
+    _need_gcc()
+    src = tmp_path / ("h.c" if lang == "c" else "h.cpp")
+    src.write_text('#include "mxfa.h"\nint main(void) { return mxfa_last_error()[0] != 0; }\n')
+    cc = "gcc" if lang == "c" else "g++"
+    std = "-std=c11" if lang == "c" else "-std=c++17"
+    subprocess.run([cc, std, "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                    str(src)], check=True, capture_output=True, text=True)
+
+
+def test_c_caller_host_checks(tmp_path):
+    exe = _build_caller(tmp_path)
+    r = subprocess.run([exe, "checks"], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.startswith("mxfa ")
+
+
+def _save(d, name, t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    (d / name).write_bytes(t.numpy().tobytes())
+
+
+@pytest.mark.gpu
+def test_c_caller_matches_python_binding(tmp_path):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mx.load_library()
+    exe = _build_caller(tmp_path)
+    dev = torch.device("cuda:0")
+
+    # Dense causal prefill, GQA, ragged tiles.
+    b, sq, sk, hq, hkv, d = 2, 300, 333, 4, 2, 128
+    p = workloads.make_problem(7400, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=[sq] * b,
+                               lens_k=[sk] * b, dense=True)
+    fd = tmp_path / "fwd"
+    fd.mkdir()
+    for x in "qkv":
+        _save(fd, f"{x}.bin", p[x])
+    scale = d ** -0.5
+    (fd / "args.txt").write_text(f"{b} {sq} {sk} {hq} {hkv} {d} 1 -1 -1 0.0 {scale!r}\n")
+    print("[c-abi] fwd", flush=True)
+    r = subprocess.run([exe, "fwd", str(fd)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    o, lse = mx.mxfa_fwd(p["q"].to(dev), p["k"].to(dev), p["v"].to(dev), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    o_c = np.frombuffer((fd / "o.bin").read_bytes(), dtype=np.int16).reshape(b, sq, hq, d)
+    l_c = np.frombuffer((fd / "lse.bin").read_bytes(), dtype=np.float32).reshape(b, hq, sq)
+    assert np.array_equal(o_c, o.cpu().view(torch.int16).numpy())
+    assert np.array_equal(l_c, lse.cpu().numpy())
+
+    # Latent split-KV decode.
+    lq, lk, hq, hkv, splits = [4, 1, 3], [700, 64, 300], 16, 1, 3
+    p = workloads.make_problem(7401, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    dd = tmp_path / "decode"
+    dd.mkdir()
+    _save(dd, "q.bin", p["q"])
+    _save(dd, "kv.bin", p["kv"])
+    _save(dd, "cu_q.bin", p["cu_seqlens_q"])
+    _save(dd, "cu_k.bin", p["cu_seqlens_k"])
+    scale = 1.0 / math.sqrt(576)
+    tq, tk = sum(lq), sum(lk)
+    (dd / "args.txt").write_text(f"{len(lq)} {max(lq)} {max(lk)} {tq} {tk} {hq} {hkv} 0 -1 -1 0.0 {scale!r} {splits}\n")
+    print("[c-abi] decode", flush=True)
+    r = subprocess.run([exe, "decode", str(dd)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    o, lse = mx.mxfa_decode_splitkv(p["q"].to(dev), p["kv"].to(dev), p["cu_seqlens_q"].to(dev),
+                                    p["cu_seqlens_k"].to(dev), max(lq), max(lk), scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    o_c = np.frombuffer((dd / "o.bin").read_bytes(), dtype=np.int16).reshape(tq, hq, 512)
+    l_c = np.frombuffer((dd / "lse.bin").read_bytes(), dtype=np.float32).reshape(hq, tq)
+    assert np.array_equal(o_c, o.cpu().view(torch.int16).numpy())
+    assert np.array_equal(l_c, lse.cpu().numpy())
