@@ -579,6 +579,22 @@ def test_decode_long_context():
     compare(o_g[rows[:, 0], rows[:, 1]], lse_g.T[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "long context")
 
 
+@pytest.mark.parametrize("window,cap", [((-1, -1), 0.0), ((4096, 0), 30.0)])
+def test_prefill_long_context(window, cap):
+    # Chunked prefill against 131072 and 100003 keys per segment (packed, GQA):
+    # large offsets, thousands of tiles per work group, checked on sampled rows
+    # (first, last and tile-edge rows of each segment included).
+    lq, lk = [200, 77], [131072, 100003]
+    p = workloads.make_problem(3820, dtype="bf16", heads_q=8, heads_kv=2, d_qk=128, d_v=128, lens_q=lq, lens_k=lk)
+    scale = 128 ** -0.5
+    print(f"[prefill] long context window={window} cap={cap}", flush=True)
+    o_g, lse_g = gpu_varlen(p, causal=True, window=window, softcap=cap, scale=scale)
+    rows = sample_rows(lq, 8, 48, seed=3821)
+    o_ref, lse_ref, _ = oracle_varlen(p, causal=True, window=window, softcap=cap, scale=scale, rows=rows)
+    compare(o_g[rows[:, 0], rows[:, 1]], lse_g.T[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16",
+            f"long context {window} {cap}")
+
+
 def test_gqa_decode_long_context():
     lq, lk = [1, 2], [65536, 40000]
     p = workloads.make_problem(3810, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=lq, lens_k=lk)
