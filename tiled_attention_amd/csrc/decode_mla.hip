@@ -144,8 +144,11 @@ void decode_split_kernel(const DecodeParams p) {
             u32x4_t v = {0u, 0u, 0u, 0u};
             if (row_valid) v = load_u32x4(qp + ks * 16);
             qreg[ks] = __builtin_bit_cast(bf16x8_t, v);
-            asm volatile("" : "+a"(qreg[ks]));
         }
+        // Moved to accumulation registers only after every load is issued: a
+        // move right after each load made each load wait for the one before.
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" : "+a"(qreg[ks]));
     }
 
     // K operand (A of S^T = K Q^T): key lr, logical chunk 36*ch + 2*ks + lh,
