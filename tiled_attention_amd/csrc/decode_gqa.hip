@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
             s[r] = x;
             mt = fmaxf(mt, x);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = half_max(mt);
         const bool grow = mt > m_run + kLazyRescale;
         if (wave_any(grow)) {
             const float m_new = grow ? mt : m_run;
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
 
     // Merge the two waves: M = max of the waves' maxima, each accumulator
     // scaled by exp2(m_w - M), L = sum of the scaled row sums.
-    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float l_row = half_sum(l_part);
     if (lh == 0) {
         sML[w][0][lr] = m_run;
         sML[w][1][lr] = l_row;

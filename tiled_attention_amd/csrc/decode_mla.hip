@@ -117,7 +117,6 @@ void decode_split_kernel(const DecodeParams p) {
 
     // This wave's row block and this lane's row.
     const int brow0 = row0 + 32 * rb;
-    const bool block_active = brow0 < nrows;
     const int my_row = brow0 + lr;
     const bool row_valid = my_row < nrows;
     const int my_tok = my_row / G;
@@ -374,7 +373,7 @@ void decode_split_kernel(const DecodeParams p) {
             float mt = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = half_max(mt);
             const float m_new = fmaxf(m_run, mt);
             alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
             m_run = m_new;
@@ -437,10 +436,8 @@ void decode_split_kernel(const DecodeParams p) {
         int phys_fill = page_of(kt0 + 3 * BN);  // page of the tile the next step issues
         asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's loads of tile 0
         lds_barrier();
-        if (block_active) {
-            s_mine = qk_tile(sT0);
-            publish();
-        }
+        s_mine = qk_tile(sT0);
+        publish();
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's loads of tile 1
         lds_barrier();
         // Step j: add the partner's partial scores of tile j; compute this
@@ -463,24 +460,21 @@ void decode_split_kernel(const DecodeParams p) {
             const __amdgpu_buffer_rsrc_t rfill = tile_rsrc(kt_fill, phys_fill);
             phys_fill = page_of(kt_fill + BN);
             issue_part(rfill, prv, 0, 3);
-            if (block_active) {
-                // On the last step this reads a finished (zero-filled) tile;
-                // the result is not used.
-                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha,
-                                    [&]() __attribute__((always_inline)) { issue_part(rfill, prv, 3, 6); });
-            } else {
-                issue_part(rfill, prv, 3, 6);
-            }
+            // Every wave runs the same code (a row block past the group's rows
+            // sees no key, so its results stay zero and are never read): the
+            // compiler then keeps an exact count of the LDS reads in flight.
+            // On the last step the scores are of a finished (zero-filled)
+            // tile and are not used.
+            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha,
+                                [&]() __attribute__((always_inline)) { issue_part(rfill, prv, 3, 6); });
             lds_barrier();
             issue_part(rfill, prv, 6, LOADS);
-            if (block_active) {
-                if (j + 1 < ntiles) publish();
-                if (wave_any(alpha != 1.0f)) {
+            publish();
+            if (wave_any(alpha != 1.0f)) {
 #pragma unroll
-                    for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
-                }
-                pv_tile(cur, pk);
+                for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
             }
+            pv_tile(cur, pk);
             asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
             lds_barrier();
         };
@@ -512,10 +506,8 @@ void decode_split_kernel(const DecodeParams p) {
         store8(R0, sT0);
         store8(R1, sT1);
         lds_barrier();
-        if (block_active) {
-            s_mine = qk_tile(sT0);
-            publish();
-        }
+        s_mine = qk_tile(sT0);
+        publish();
         lds_barrier();
         // Step j: loads of tile j+4 into the registers of tile j (converted in
         // step j-2); scores of tile j+1 with the softmax of tile j; barrier;
@@ -529,17 +521,14 @@ void decode_split_kernel(const DecodeParams p) {
             uint32_t pk[8];
             float alpha = 1.0f;
             load8(kt0 + (j + 4) * BN, rl);
-            if (block_active)
-                s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, []() __attribute__((always_inline)) {});
+            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, []() __attribute__((always_inline)) {});
             lds_barrier();
-            if (block_active) {
-                if (j + 1 < ntiles) publish();
-                if (wave_any(alpha != 1.0f)) {
+            publish();
+            if (wave_any(alpha != 1.0f)) {
 #pragma unroll
-                    for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
-                }
-                pv_tile(cur, pk);
+                for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
             }
+            pv_tile(cur, pk);
             store8(rc, fill);
             lds_barrier();
         };
@@ -564,7 +553,7 @@ void decode_split_kernel(const DecodeParams p) {
     // Partial (m, l, acc) of this split: row 32*rb + lr of the group, channels
     // 256*ch + 32*cb + 8*(r/4) + 4*lh + r%4.
     const long long pidx = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits + sp;
-    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float l_row = half_sum(l_part);
     const int grow_idx = 32 * rb + lr;
     float* pacc = p.part_acc + (pidx * ROWS + grow_idx) * DV + 256 * ch + 4 * lh;
 #pragma unroll

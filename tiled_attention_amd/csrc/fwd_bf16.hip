@@ -264,7 +264,7 @@ void fwd_bf16_kernel(const FwdParams p) {
                 m = fmaxf(m, x);
             }
         }
-        m = fmaxf(m, __shfl_xor(m, 32));
+        m = half_max(m);
         if constexpr (kMode == 0) m *= c_exp;
         return m;
     };
@@ -317,7 +317,7 @@ void fwd_bf16_kernel(const FwdParams p) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = half_max(mt);
             if constexpr (kMode == 0) mt *= c_exp;
             const float m_new = fmaxf(m_run, mt);
             const float alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
@@ -531,7 +531,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     }
 
     // Epilogue: combine the two lane halves' sums, normalise, store.
-    const float l_row = l_part + __shfl_xor(l_part, 32);
+    const float l_row = half_sum(l_part);
     if (!q_valid) return;
     const float inv = (l_row > 0.0f) ? 1.0f / l_row : 0.0f;
     uint16_t* O = static_cast<uint16_t*>(p.o) + (long long)(q_start + qi) * q_tok + (long long)h * D;

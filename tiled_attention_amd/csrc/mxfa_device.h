@@ -142,7 +142,12 @@ MXFA_DEV u32x2_t lds_read_tr16(const void* p) {
 // Work-group barrier that orders LDS traffic only: this wave's LDS accesses
 // complete, then s_barrier. Unlike __syncthreads() it does not wait for
 // outstanding global loads (e.g. the next tile streaming into LDS).
-MXFA_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+MXFA_DEV void lds_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 MXFA_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)(p); }
 
@@ -251,6 +256,18 @@ MXFA_DEV u32x4_t lds_read16(const void* p) {
 
 MXFA_DEV u32x4_t lds_load16(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((size_t)addr);
+}
+
+// Combine a value with the one of lane l ^ 32 (the two halves of the wave
+// swapped in registers with v_permlane32_swap; no LDS instruction, so the
+// compiler's count of outstanding LDS reads stays exact across branches).
+MXFA_DEV float half_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+MXFA_DEV float half_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 MXFA_DEV bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
