@@ -94,9 +94,16 @@ def work_of(w, inp):
     return pairs, flops, q_b + kv_b + o_b + lse_b
 
 
+# Headers every kernel source includes: a change there changes the kernels too.
+SHARED_SOURCES = ("tiled_attention_amd/csrc/mxfa_device.h", "tiled_attention_amd/csrc/mxfa_internal.h")
+
+
 def source_sha(name):
-    with open(os.path.join(ROOT, KERNEL_SOURCES[name]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[name],) + SHARED_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # rocprofv3 kernel names of each kernel family (one launch of mxfa_decode_splitkv
