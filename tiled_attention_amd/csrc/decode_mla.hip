@@ -496,31 +496,32 @@ void decode_split_kernel(const DecodeParams p) {
         // Drain the look-ahead loads before the work group's LDS is released.
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
-        // fp8 rows: tile j is loaded into registers in step j-4 (set j % 4)
-        // and converted into its LDS stage j % 4 at the end of step j-2.
-        Raw8 R0, R1, R2, R3;
+        // fp8 rows: tile j is loaded into registers in step j-3 (set j % 3)
+        // and converted into its LDS stage j % 3 at the end of step j-2: two
+        // steps of load latency covered with three register sets (a fourth
+        // set left too few registers for the P V reads to run ahead).
+        Raw8 R0, R1, R2;
         load8(kt0, R0);
         load8(kt0 + BN, R1);
         load8(kt0 + 2 * BN, R2);
-        load8(kt0 + 3 * BN, R3);
         store8(R0, sT0);
         store8(R1, sT1);
         lds_barrier();
         s_mine = qk_tile(sT0);
         publish();
         lds_barrier();
-        // Step j: loads of tile j+4 into the registers of tile j (converted in
-        // step j-2); scores of tile j+1 with the softmax of tile j; barrier;
-        // publish, P V of tile j; tile j+2 converted into the stage of tile
-        // j-2 (last read in step j-2); barrier.
+        // Step j: loads of tile j+3 into the registers of tile j (converted
+        // at the end of step j-2); scores of tile j+1 with the softmax of tile
+        // j; barrier; publish, P V of tile j; tile j+2 converted into the
+        // stage of tile j-1 (last read in step j-1); barrier.
         auto step8 = [&](auto stage_tag, int j, Raw8& rl, const Raw8& rc) __attribute__((always_inline)) {
             constexpr int S = decltype(stage_tag)::value;
-            char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : S == 2 ? sT2 : sT3;
-            char* const nxt = S == 0 ? sT1 : S == 1 ? sT2 : S == 2 ? sT3 : sT0;
-            char* const fill = S == 0 ? sT2 : S == 1 ? sT3 : S == 2 ? sT0 : sT1;
+            char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : sT2;
+            char* const nxt = S == 0 ? sT1 : S == 1 ? sT2 : sT0;
+            char* const fill = S == 0 ? sT2 : S == 1 ? sT0 : sT1;
             uint32_t pk[8];
             float alpha = 1.0f;
-            load8(kt0 + (j + 4) * BN, rl);
+            load8(kt0 + (j + 3) * BN, rl);
             s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, []() __attribute__((always_inline)) {});
             lds_barrier();
             publish();
@@ -535,17 +536,14 @@ void decode_split_kernel(const DecodeParams p) {
         using st0 = std::integral_constant<int, 0>;
         using st1 = std::integral_constant<int, 1>;
         using st2 = std::integral_constant<int, 2>;
-        using st3 = std::integral_constant<int, 3>;
         int j = 0;
-        for (; j + STAGES <= ntiles; j += STAGES) {
+        for (; j + 3 <= ntiles; j += 3) {
             step8(st0{}, j, R0, R2);
-            step8(st1{}, j + 1, R1, R3);
-            step8(st2{}, j + 2, R2, R0);
-            step8(st3{}, j + 3, R3, R1);
+            step8(st1{}, j + 1, R1, R0);
+            step8(st2{}, j + 2, R2, R1);
         }
         if (j < ntiles) step8(st0{}, j, R0, R2);
-        if (j + 1 < ntiles) step8(st1{}, j + 1, R1, R3);
-        if (j + 2 < ntiles) step8(st2{}, j + 2, R2, R0);
+        if (j + 1 < ntiles) step8(st1{}, j + 1, R1, R0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
     }
