@@ -459,6 +459,11 @@ void decode_split_kernel(const DecodeParams p) {
             float alpha = 1.0f;
             const __amdgpu_buffer_rsrc_t rfill = tile_rsrc(kt_fill, phys_fill);
             phys_fill = page_of(kt_fill + BN);
+            // Wait for the page-table read here, where no LDS read is in
+            // flight: the scalar load shares the LDS wait counter and returns
+            // out of order, so while it is pending every LDS wait of the step
+            // would have to drain all reads.
+            if constexpr (kPaged) asm volatile("" : "+s"(phys_fill));
             issue_part(rfill, prv, 0, 3);
             // Every wave runs the same code (a row block past the group's rows
             // sees no key, so its results stay zero and are never read): the
