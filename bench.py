@@ -26,8 +26,8 @@ separately, ``--pmc WRITE_SIZE`` with ``--copy-probe-mb N`` (a device copy of
 N MiB after the workloads, whose counter readings calibrate the counters),
 then ``python bench.py --pmc-summarize FETCH_CSV WRITE_CSV --copy-probe-mb N``
 writes profiles/pmc_traffic.json: measured HBM bytes per launch for each
-kernel, tagged with the hash of the kernel's source (ignored once the source
-changes).
+kernel, tagged with a hash of the kernel's code (comments and whitespace
+aside; the figures are ignored once that code changes).
 """
 from __future__ import annotations
 
@@ -98,11 +98,36 @@ def work_of(w, inp):
 SHARED_SOURCES = ("tiled_attention_amd/csrc/mxfa_device.h", "tiled_attention_amd/csrc/mxfa_internal.h")
 
 
+def _code_only(text):
+    """C++ source without comments and whitespace (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_sha(name):
+    """Hash of the code (comments and whitespace aside) of a kernel's source and the shared headers."""
     h = hashlib.sha256()
     for rel in (KERNEL_SOURCES[name],) + SHARED_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -14,7 +14,8 @@
 // stages (32-key tiles) filled by buffer loads that write LDS directly; each
 // wave waits only for the tile it needs (vmcnt with the count of later
 // loads). The steps are software pipelined: while tile j's P V runs, tile
-// j+1 is read for its scores and tiles j+2 and j+3 stream in.
+// j+1 is read for its scores and tiles j+2 and j+3 stream in. An fp8 cache
+// takes three stages instead, filled from registers (see the fp8 path).
 // Wave w = (rb, ch) with rb = w % 2 (rows 32*rb..+31) and ch = w / 2:
 //   QK: the partial S^T (32 keys x 32 rows) over channels 288*ch..+287 with
 //       18 v_mfma_f32_32x32x16_bf16 (its Q^T slice lives in accumulation
