@@ -361,6 +361,12 @@ void fwd_bf16_kernel(const FwdParams p) {
         for (int m = 0; m < AHEAD; ++m) a[m] = rd(m);
         const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
         float psum = 0.0f;
+        // Raised issue priority for this phase: where the two waves sharing a
+        // SIMD (one from each work group) are both ready, the one in its
+        // exponential phase goes first, and its vector work then fills the
+        // other wave's MFMA time (3-4% faster on the causal and chunked
+        // prefill workloads).
+        __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -378,6 +384,7 @@ void fwd_bf16_kernel(const FwdParams p) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         return psum;
     };
     // Phase B, fused: O += V_j P_j on the MFMAs while the vector ALU takes
