@@ -248,8 +248,10 @@ class Runner:
             mq, mk = max(inp["lens_q"]), max(inp["lens_k"])
             o = torch.empty_like(q)
             lse = torch.empty((w.heads_q, q.shape[0]), dtype=torch.float32, device=dev)
+            nbytes = mx.mxfa_fwd_varlen_workspace_bytes(w.batch, mq, w.heads_q, w.d_qk)
+            ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
             self.call = lambda: mx.mxfa_fwd_varlen(q, k, v, cq, ck, mq, mk, causal=w.causal, window=w.window,
-                                                   softcap=w.softcap, scale=scale, out=o, lse=lse)
+                                                   softcap=w.softcap, scale=scale, workspace=ws, out=o, lse=lse)
             self.kernel = "fwd_bf16"
         else:
             q = inp["q"].to(dev)
@@ -283,21 +285,127 @@ class Runner:
             del inp
         torch.cuda.synchronize()
 
-    def time(self, steps, warmup):
+    def time(self, steps, warmup, repeats=1, sampler=None):
+        """ms per call of each of ``repeats`` timed regions of exactly ``steps`` calls.
+
+        ``warmup`` untimed calls come first. Each region is bracketed by HIP
+        events on the stream the calls are launched on, with a device
+        synchronisation on both sides. ``sampler`` (a ClockSampler) reads the
+        shader clock while the regions run.
+        """
         import torch
 
         for _ in range(warmup):
             self.call()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(steps):
-            self.call()
-        end.record(stream)
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / steps  # ms per call
+        out = []
+        if sampler:
+            sampler.start()
+        try:
+            for _ in range(repeats):
+                start = torch.cuda.Event(enable_timing=True)
+                end = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                start.record(stream)
+                for _ in range(steps):
+                    self.call()
+                end.record(stream)
+                torch.cuda.synchronize()
+                out.append(start.elapsed_time(end) / steps)  # ms per call
+        finally:
+            if sampler:
+                sampler.stop()
+        return out
+
+
+class ClockSampler:
+    """The GPU's shader (GFX) clock as the driver reports it, read through amdsmi
+    from a host thread while timed regions run.
+
+    The device is matched to cuda:0 by its PCI address. When amdsmi is missing
+    or cannot read the device, ``summary()`` says so instead of giving figures.
+    """
+
+    def __init__(self):
+        self.handle, self.reason = None, None
+        self.samples = []
+        self._stop = None
+        self._thread = None
+        try:
+            import amdsmi
+            import torch
+
+            amdsmi.amdsmi_init()
+            props = torch.cuda.get_device_properties(0)
+            want = (int(getattr(props, "pci_domain_id", 0)), int(props.pci_bus_id), int(props.pci_device_id))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, devfn = bdf.split(":")
+                if (int(dom, 16), int(bus, 16), int(devfn.split(".")[0], 16)) == want:
+                    self.handle = h
+                    break
+            if self.handle is None:
+                self.reason = f"no amdsmi device at PCI {want}"
+            else:
+                self._read()  # one read up front, so that an unreadable clock shows here
+            self._amdsmi = amdsmi
+        except Exception as e:  # noqa: BLE001 - any failure only means "no clock figure"
+            self.handle, self.reason = None, f"amdsmi unavailable: {type(e).__name__}: {e}"
+
+    def _read(self):
+        import amdsmi
+
+        return float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+
+    def start(self):
+        import threading
+
+        if self.handle is None:
+            return
+        self.samples = []
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception:  # noqa: BLE001
+                    return
+                self._stop.wait(0.0005)
+
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        if self.handle is None or not self.samples:
+            return {"mhz": None, "note": self.reason or "no samples"}
+        xs = sorted(self.samples)
+        return {"mhz": round(float(np.median(xs)), 1), "min": xs[0], "max": xs[-1], "samples": len(xs),
+                "source": "amdsmi GFX clock, sampled by a host thread during the timed regions"}
+
+
+def clock_fields(res, peak):
+    """Shader clock seen during the timed regions, and the MFMA peak scaled to it.
+
+    The dense bf16 MFMA peak assumes 2.4 GHz; at a lower clock the chip's
+    attainable peak is lower in proportion.
+    """
+    mhz = (res.get("clock") or {}).get("mhz")
+    out = {"clock_mhz": mhz, "peak_clock_mhz": 2400.0}
+    if mhz:
+        peak_at = peak * mhz / 2400.0
+        out["peak_at_clock"] = round(peak_at, 1)
+        out["frac_at_clock"] = round(res["tflops"] / peak_at, 4)
+    else:
+        out["clock_note"] = (res.get("clock") or {}).get("note")
+    return out
 
 
 def cpu_baseline(name, target_s):
@@ -356,9 +464,14 @@ def cpu_baseline(name, target_s):
         rate = done / max(elapsed, 1e-9)
         n = int(min(total_rows - done, max(256, rate * (target_s - elapsed))))
     flops = pairs * 2 * (w.d_qk + w.d_v)
+    _, _, call_bytes = work_of(w, inp)
     return {
+        "workload": name,
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
+        "gflops": round(flops / elapsed / 1e9, 2),
+        # algorithmic bytes of the sampled share of one call, per second
+        "gbs": round(call_bytes * done / total_rows / elapsed / 1e9, 3),
         "cores": threads,
         "kind": "oracle",
         "sample": f"{done} of {total_rows} (token, head) rows of {name}, seeded random order; "
@@ -384,8 +497,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed regions of --steps calls each; the figures are their median")
     ap.add_argument("--workloads", default=f"{PRIMARY},{DECODE}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="do not sample the shader clock")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -413,14 +529,19 @@ def main():
     if PRIMARY not in names:
         names.insert(0, PRIMARY)
 
+    sampler = None if args.no_clock else ClockSampler()
     results = {}
     for name in names:
         print(f"[bench] {name}: preparing inputs", file=sys.stderr, flush=True)
         r = Runner(name)
-        ms = r.time(args.steps, args.warmup)
+        reps = r.time(args.steps, args.warmup, max(1, args.repeats), sampler)
+        ms = float(np.median(reps))
         res = {
             "workload": name,
             "ms": round(ms, 4),
+            "ms_mean": round(float(np.mean(reps)), 4),
+            "ms_repeats": [round(x, 4) for x in reps],
+            "clock": sampler.summary() if sampler else None,
             "tflops": r.flops / (ms * 1e-3) / 1e12,
             "gbs": r.bytes / (ms * 1e-3) / 1e9,
             "flops_per_call": r.flops,
@@ -430,8 +551,9 @@ def main():
         if r.w.kind in ("decode", "gqa_decode"):
             res["splits"] = r.splits
         results[name] = res
-        print(f"[bench] {name}: {ms:.4f} ms/call, {res['tflops']:.1f} TFLOP/s, {res['gbs']:.1f} GB/s",
-              file=sys.stderr, flush=True)
+        clk = (res["clock"] or {}).get("mhz")
+        print(f"[bench] {name}: {ms:.4f} ms/call (median of {len(reps)} x {args.steps}; mean {res['ms_mean']:.4f}), "
+              f"{res['tflops']:.1f} TFLOP/s, {res['gbs']:.1f} GB/s, clock {clk} MHz", file=sys.stderr, flush=True)
         del r
         torch.cuda.empty_cache()
 
@@ -472,6 +594,10 @@ def main():
             "traffic": load_traffic(p["kernel"]),
             "kernel": p["kernel"],
             "flops_per_launch": p["flops_per_call"],
+            "ms_median": p["ms"],
+            "ms_mean": p["ms_mean"],
+            "repeats": len(p["ms_repeats"]),
+            **clock_fields(p, PEAK_BF16_TFLOPS),
         },
     }
     if DECODE in results:
@@ -484,8 +610,10 @@ def main():
             "splits": d.get("splits"),
             "roofline": {"bound": "hbm", "achieved": round(d["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(d["gbs"] / PEAK_HBM_GBS, 4), "traffic": load_traffic("decode_mla"),
-                         "bytes_per_launch": d["bytes_per_call"],
-                         "note": "one call = split kernel + combine kernel"},
+                         "bytes_per_launch": d["bytes_per_call"], "ms_median": d["ms"], "ms_mean": d["ms_mean"],
+                         "repeats": len(d["ms_repeats"]), "clock_mhz": (d["clock"] or {}).get("mhz"),
+                         "note": "one call = split kernel + combine kernel; the HBM peak does not scale "
+                                 "with the shader clock"},
         }
     extra = [v for k, v in results.items() if k not in (PRIMARY, DECODE)]
     if extra:
@@ -493,6 +621,13 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: fp64 oracle on a sample of the prefill workload", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(PRIMARY, args.cpu_seconds)
+        # The same oracle on bounded samples of the packed GQA prefill and the
+        # latent decode (reported only; the headline figure is the prefill's).
+        others = []
+        for name in ("varlen_gqa_causal_bf16", DECODE):
+            print(f"[bench] cpu baseline: fp64 oracle on a sample of {name}", file=sys.stderr, flush=True)
+            others.append(cpu_baseline(name, args.cpu_seconds / 2))
+        line["cpu_baseline"]["others"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -24,8 +24,11 @@
  *    attention; flash_attention_gqa on the oxillama-runtime page).
  *  - A row that sees no key gets O = 0 and LSE = -inf.
  *  - LSE is float32, natural log.
- *  - bf16 inputs: products accumulate in fp32; O is rounded to bf16 with
- *    round-to-nearest-even. f32 inputs: fp32 throughout.
+ *  - bf16 inputs: products accumulate in fp32; the softmax weights p enter
+ *    the P V product rounded to bf16, and O is divided by the sum of those
+ *    rounded weights (so a row's weights sum to one), the LSE taken from the
+ *    fp32 sum of p; O is rounded to bf16 with round-to-nearest-even. f32
+ *    inputs: fp32 throughout.
  *
  * Ownership and execution
  * -----------------------
@@ -93,7 +96,14 @@ mxfa_status mxfa_fwd(const void* q, const void* k, const void* v, void* o, float
  *   o   [total_q, heads_q,  head_dim]      lse  [heads_q, total_q] float32 (may be NULL)
  *   cu_seqlens_q, cu_seqlens_k: int32 device arrays of batch + 1 entries.
  * max_seqlen_q / max_seqlen_k must bound every segment's length (they size the
- * launch; a segment longer than max_seqlen_q is not fully computed).
+ * work list; rows of a segment longer than max_seqlen_q may be left unwritten).
+ * workspace: device memory of at least mxfa_fwd_varlen_workspace_bytes()
+ * bytes for the same batch and max_seqlen_q, 16-byte aligned; owned by the
+ * caller, overwritten (nothing in it needs clearing), not needed after the
+ * stream passes the call. A first small kernel walks cu_seqlens on the device
+ * and writes the list of (segment, query tile) pairs there, longest causal
+ * work first; the forward kernel then runs exactly those tiles. Too small a
+ * workspace: MXFA_ERR_WORKSPACE, nothing enqueued.
  * Other arguments as for mxfa_fwd.
  */
 mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -101,7 +111,17 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
                             int heads_q, int heads_kv, int head_dim, mxfa_dtype dtype, int causal,
                             int window_left, int window_right, float softcap, float scale,
-                            mxfa_stream_t stream);
+                            void* workspace, size_t workspace_bytes, mxfa_stream_t stream);
+
+/*
+ * Workspace bytes mxfa_fwd_varlen needs (0 when batch or max_seqlen_q is 0):
+ * a count, batch + 1 prefix sums and one (segment, q tile) pair per query
+ * tile of batch segments of max_seqlen_q tokens, for either dtype. heads_q
+ * and head_dim do not change it (every query head reads the same list); they
+ * are part of the signature so that a future kernel may depend on them.
+ * Host-only arithmetic, no device query.
+ */
+size_t mxfa_fwd_varlen_workspace_bytes(int batch, int max_seqlen_q, int heads_q, int head_dim);
 
 /*
  * Split-KV decode over a shared latent KV (the kernelbot amd-mixed-mla

@@ -6,12 +6,18 @@
  *   caller checks          host-side argument checks and the version string
  *                          (no device work; runs without a GPU)
  *   caller fwd <dir>       dense forward (bf16) on the inputs in <dir>
- *   caller decode <dir>    latent split-KV decode (bf16) on the inputs in <dir>
+ *   caller varlen <dir>    packed forward (bf16), work list in a workspace
+ *   caller decode <dir>    latent split-KV decode (bf16)
+ *   caller fp8 <dir>       latent split-KV decode over an e4m3 cache
+ *   caller paged <dir>     latent split-KV decode over a paged cache
+ *   caller gqa <dir>       standard-head split-KV decode (bf16)
  *
  * <dir>/args.txt holds the call's integer and float arguments (see below);
- * the tensors are raw little-endian files (q.bin, k.bin, v.bin or kv.bin,
- * cu_q.bin, cu_k.bin). o.bin and lse.bin are written back. Work runs on a
- * stream the program creates. Exit status 0 on success.
+ * the tensors are raw little-endian files (q.bin, k.bin, v.bin, kv.bin,
+ * cu_q.bin, cu_k.bin, seqlens.bin, table.bin as the call needs). o.bin and
+ * lse.bin are written back. Work runs on a stream the program creates; every
+ * workspace size comes from the library's own size query. Exit status 0 on
+ * success.
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -81,6 +87,10 @@ static int checks(void) {
         return 4;
     if (mxfa_fwd(a, a, a, a, NULL, 0, 4, 4, 2, 1, 128, MXFA_BF16, 1, -1, -1, 0.0f, 0.1f, NULL) != MXFA_OK)
         return 5;
+    if (mxfa_fwd_varlen(a, a, a, a, NULL, (const int32_t*)a, (const int32_t*)a, 2, 16, 16, 20, 20, 4, 2, 128,
+                        MXFA_BF16, 1, -1, -1, 0.0f, 0.1f, a, mxfa_fwd_varlen_workspace_bytes(2, 16, 4, 128) - 1,
+                        NULL) != MXFA_ERR_WORKSPACE)
+        return 6;
     printf("%s\n", mxfa_version());
     return 0;
 }
@@ -122,33 +132,92 @@ static int run(const char* mode, const char* dir) {
         hipFree(v);
         hipFree(o);
         hipFree(lse);
-    } else {
-        /* batch mq mk tq tk hq hkv causal wl wr softcap scale splits */
-        int b, mq, mk, tq, tk, hq, hkv, causal, wl, wr, splits;
+    } else if (strcmp(mode, "varlen") == 0 || strcmp(mode, "gqa") == 0) {
+        /* batch mq mk tq tk hq hkv d causal wl wr softcap scale splits */
+        int b, mq, mk, tq, tk, hq, hkv, d, causal, wl, wr, splits;
         float cap, scale;
-        if (sscanf(text, "%d %d %d %d %d %d %d %d %d %d %f %f %d", &b, &mq, &mk, &tq, &tk, &hq, &hkv, &causal, &wl,
-                   &wr, &cap, &scale, &splits) != 13)
+        if (sscanf(text, "%d %d %d %d %d %d %d %d %d %d %d %f %f %d", &b, &mq, &mk, &tq, &tk, &hq, &hkv, &d, &causal,
+                   &wl, &wr, &cap, &scale, &splits) != 14)
             return 12;
-        size_t nq, nkv, ncq, nck;
+        const int is_gqa = strcmp(mode, "gqa") == 0;
+        size_t nq, nk, nv, ncq, nck;
+        void* q = upload(dir, "q.bin", &nq);
+        void* k = upload(dir, "k.bin", &nk);
+        void* v = upload(dir, "v.bin", &nv);
+        int32_t* cq = upload(dir, "cu_q.bin", &ncq);
+        int32_t* ck = upload(dir, "cu_k.bin", &nck);
+        const size_t ws_bytes = is_gqa ? mxfa_decode_splitkv_gqa_workspace_bytes(b, mq, mk, hq, hkv, d, splits)
+                                       : mxfa_fwd_varlen_workspace_bytes(b, mq, hq, d);
+        const size_t no = nq, nl = (size_t)hq * tq * sizeof(float);
+        void *o = NULL, *ws = NULL;
+        float* lse = NULL;
+        if (!q || !k || !v || !cq || !ck || hipMalloc(&o, no ? no : 16) != hipSuccess ||
+            hipMalloc((void**)&lse, nl ? nl : 16) != hipSuccess || hipMalloc(&ws, ws_bytes ? ws_bytes : 16) != hipSuccess)
+            return 13;
+        if (is_gqa)
+            st = mxfa_decode_splitkv_gqa(q, k, v, o, lse, cq, ck, b, mq, mk, tq, tk, hq, hkv, d, causal, wl, wr, cap,
+                                         scale, splits, ws, ws_bytes, (mxfa_stream_t)stream);
+        else
+            st = mxfa_fwd_varlen(q, k, v, o, lse, cq, ck, b, mq, mk, tq, tk, hq, hkv, d, MXFA_BF16, causal, wl, wr,
+                                 cap, scale, ws, ws_bytes, (mxfa_stream_t)stream);
+        if (st == MXFA_OK && hipStreamSynchronize(stream) == hipSuccess)
+            rc = download(dir, "o.bin", o, no) || download(dir, "lse.bin", lse, nl);
+        hipFree(q);
+        hipFree(k);
+        hipFree(v);
+        hipFree(cq);
+        hipFree(ck);
+        hipFree(o);
+        hipFree(lse);
+        hipFree(ws);
+    } else {
+        /* decode, fp8: batch mq mk tq tk hq hkv causal wl wr softcap scale splits kv_scale
+         * paged:       batch mq mk tq num_pages page_size max_pages hq hkv causal wl wr softcap scale splits */
+        const int paged = strcmp(mode, "paged") == 0, fp8 = strcmp(mode, "fp8") == 0;
+        int b, mq, mk, tq, tk = 0, hq, hkv, causal, wl, wr, splits, num_pages = 0, page_size = 0, max_pages = 0;
+        float cap, scale, kv_scale = 1.0f;
+        if (paged) {
+            if (sscanf(text, "%d %d %d %d %d %d %d %d %d %d %d %d %f %f %d", &b, &mq, &mk, &tq, &num_pages, &page_size,
+                       &max_pages, &hq, &hkv, &causal, &wl, &wr, &cap, &scale, &splits) != 15)
+                return 12;
+        } else {
+            /* kv_scale is optional for the bf16 decode */
+            const int got = sscanf(text, "%d %d %d %d %d %d %d %d %d %d %f %f %d %f", &b, &mq, &mk, &tq, &tk, &hq,
+                                   &hkv, &causal, &wl, &wr, &cap, &scale, &splits, &kv_scale);
+            if (got != 14 && !(got == 13 && !fp8)) return 12;
+        }
+        size_t nq, nkv, ncq, nck = 0, nsl = 0, ntb = 0;
         void* q = upload(dir, "q.bin", &nq);
         void* kv = upload(dir, "kv.bin", &nkv);
         int32_t* cq = upload(dir, "cu_q.bin", &ncq);
-        int32_t* ck = upload(dir, "cu_k.bin", &nck);
+        int32_t* ck = paged ? NULL : upload(dir, "cu_k.bin", &nck);
+        int32_t* seqlens = paged ? upload(dir, "seqlens.bin", &nsl) : NULL;
+        int32_t* table = paged ? upload(dir, "table.bin", &ntb) : NULL;
         const size_t ws_bytes = mxfa_decode_splitkv_workspace_bytes(b, mq, mk, hq, hkv, 512, splits);
         const size_t no = (size_t)tq * hq * 512 * 2, nl = (size_t)hq * tq * sizeof(float);
         void *o = NULL, *ws = NULL;
         float* lse = NULL;
-        if (!q || !kv || !cq || !ck || hipMalloc(&o, no ? no : 16) != hipSuccess ||
+        if (!q || !kv || !cq || (paged ? (!seqlens || !table) : !ck) || hipMalloc(&o, no ? no : 16) != hipSuccess ||
             hipMalloc((void**)&lse, nl ? nl : 16) != hipSuccess || hipMalloc(&ws, ws_bytes ? ws_bytes : 16) != hipSuccess)
             return 13;
-        st = mxfa_decode_splitkv(q, kv, o, lse, cq, ck, b, mq, mk, tq, tk, hq, hkv, 576, 512, causal, wl, wr, cap,
-                                 scale, splits, ws, ws_bytes, (mxfa_stream_t)stream);
+        if (paged)
+            st = mxfa_decode_splitkv_paged(q, kv, o, lse, cq, seqlens, table, b, mq, mk, tq, num_pages, page_size,
+                                           max_pages, hq, hkv, 576, 512, causal, wl, wr, cap, scale, splits, ws,
+                                           ws_bytes, (mxfa_stream_t)stream);
+        else if (fp8)
+            st = mxfa_decode_splitkv_fp8(q, kv, o, lse, cq, ck, b, mq, mk, tq, tk, hq, hkv, 576, 512, causal, wl, wr,
+                                         cap, scale, kv_scale, splits, ws, ws_bytes, (mxfa_stream_t)stream);
+        else
+            st = mxfa_decode_splitkv(q, kv, o, lse, cq, ck, b, mq, mk, tq, tk, hq, hkv, 576, 512, causal, wl, wr, cap,
+                                     scale, splits, ws, ws_bytes, (mxfa_stream_t)stream);
         if (st == MXFA_OK && hipStreamSynchronize(stream) == hipSuccess)
             rc = download(dir, "o.bin", o, no) || download(dir, "lse.bin", lse, nl);
         hipFree(q);
         hipFree(kv);
         hipFree(cq);
-        hipFree(ck);
+        if (ck) hipFree(ck);
+        if (seqlens) hipFree(seqlens);
+        if (table) hipFree(table);
         hipFree(o);
         hipFree(lse);
         hipFree(ws);
@@ -164,7 +233,9 @@ static int run(const char* mode, const char* dir) {
 
 int main(int argc, char** argv) {
     if (argc >= 2 && strcmp(argv[1], "checks") == 0) return checks();
-    if (argc >= 3 && (strcmp(argv[1], "fwd") == 0 || strcmp(argv[1], "decode") == 0)) return run(argv[1], argv[2]);
-    fprintf(stderr, "usage: caller checks | caller fwd <dir> | caller decode <dir>\n");
+    static const char* const modes[] = {"fwd", "varlen", "decode", "fp8", "paged", "gqa"};
+    for (size_t i = 0; argc >= 3 && i < sizeof modes / sizeof modes[0]; ++i)
+        if (strcmp(argv[1], modes[i]) == 0) return run(argv[1], argv[2]);
+    fprintf(stderr, "usage: caller checks | caller {fwd|varlen|decode|fp8|paged|gqa} <dir>\n");
     return 2;
 }

@@ -58,7 +58,7 @@ def _ctype_of(decl: str, named: bool = True):
 
 def test_header_declares_the_entry_points():
     names = set(_prototypes())
-    for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_decode_splitkv", "mxfa_decode_splitkv_paged",
+    for n in ("mxfa_fwd", "mxfa_fwd_varlen", "mxfa_fwd_varlen_workspace_bytes", "mxfa_decode_splitkv", "mxfa_decode_splitkv_paged",
               "mxfa_decode_splitkv_fp8",
               "mxfa_decode_splitkv_gqa", "mxfa_decode_splitkv_gqa_workspace_bytes",
               "mxfa_decode_splitkv_gqa_num_splits",
@@ -111,19 +111,34 @@ def test_fwd_host_checks(lib, kw, status):
 
 def varlen(lib, **kw):
     a = dict(q=A, k=A, v=A, o=A, lse=A, cq=A, ck=A, batch=2, mq=16, mk=16, tq=20, tk=20, hq=4, hkv=2,
-             d=64, dtype=1, causal=1, wl=-1, wr=-1, softcap=0.0, scale=0.1, stream=None)
+             d=64, dtype=1, causal=1, wl=-1, wr=-1, softcap=0.0, scale=0.1, ws=A, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.mxfa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["batch"], a["mq"],
                                a["mk"], a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["dtype"], a["causal"],
-                               a["wl"], a["wr"], a["softcap"], a["scale"], a["stream"])
+                               a["wl"], a["wr"], a["softcap"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
 
 
+# Every case fails on the host before anything is enqueued (the workspace
+# cases because it is missing, too small or misaligned), or is an empty call.
 @pytest.mark.parametrize("kw,status", [
     (dict(cq=None), INVALID), (dict(ck=A + 2), INVALID), (dict(mq=30), INVALID), (dict(tk=-1), INVALID),
     (dict(d=80), UNSUPPORTED), (dict(hq=3), INVALID), (dict(batch=0), OK), (dict(tq=0, mq=0), OK),
+    (dict(ws=None, ws_bytes=1 << 20), WORKSPACE), (dict(ws_bytes=15), WORKSPACE),
+    (dict(ws=A + 8, ws_bytes=1 << 20), INVALID), (dict(batch=0, ws=None), OK),
 ])
 def test_varlen_host_checks(lib, kw, status):
     assert varlen(lib, **kw) == status
+    if status != OK:
+        assert lib.mxfa_last_error().decode()
+
+
+@pytest.mark.parametrize("batch,mq", [(16, 3991), (1, 1), (3, 32), (3, 33), (0, 100), (5, 0)])
+def test_varlen_workspace_bytes_is_arithmetic(lib, batch, mq):
+    # count + 3 unused ints, batch + 1 prefix sums (padded to an even count),
+    # one (segment, q tile) int pair per 32-row tile of every segment.
+    want = 0 if batch == 0 or mq == 0 else 4 * (4 + ((batch + 2) & ~1)) + 8 * batch * -(-mq // 32)
+    for hq, d in ((32, 128), (4, 64)):
+        assert mx.mxfa_fwd_varlen_workspace_bytes(batch, mq, hq, d) == want
 
 
 def decode(lib, **kw):
@@ -222,7 +237,8 @@ def test_gqa_decode_host_checks(lib, kw, status):
                                                         (1, 1, 64, 8, 8, 128, 1)])
 def test_gqa_workspace_bytes_is_arithmetic(lib, batch, mq, mk, hq, hkv, d, splits):
     groups = -(-mq * (hq // hkv) // 32)
-    want = batch * hkv * groups * splits * 32 * (d + 2) * 4 if splits > 1 else 0
+    # per row: d fp32 accumulators plus (max, sum of p, sum of bf16(p))
+    want = batch * hkv * groups * splits * 32 * (d + 3) * 4 if splits > 1 else 0
     assert mx.mxfa_decode_splitkv_gqa_workspace_bytes(batch, mq, mk, hq, hkv, d, splits) == want
     assert mx.mxfa_decode_splitkv_gqa_num_splits(batch, mq, mk, hq, hkv, splits) == splits
 
@@ -231,6 +247,6 @@ def test_gqa_workspace_bytes_is_arithmetic(lib, batch, mq, mk, hq, hkv, d, split
                                                       (1, 1, 1, 16, 1, 1)])
 def test_workspace_bytes_is_arithmetic(lib, batch, mq, mk, hq, hkv, splits):
     groups = -(-mq * (hq // hkv) // 64)
-    want = batch * hkv * groups * splits * 64 * (512 + 2) * 4
+    want = batch * hkv * groups * splits * 64 * (512 + 3) * 4
     assert mx.mxfa_decode_splitkv_workspace_bytes(batch, mq, mk, hq, hkv, 512, splits) == want
     assert mx.mxfa_decode_splitkv_num_splits(batch, mq, mk, hq, hkv, splits) == splits

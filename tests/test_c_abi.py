@@ -124,3 +124,112 @@ def test_c_caller_matches_python_binding(tmp_path):
     l_c = np.frombuffer((dd / "lse.bin").read_bytes(), dtype=np.float32).reshape(hq, tq)
     assert np.array_equal(o_c, o.cpu().view(torch.int16).numpy())
     assert np.array_equal(l_c, lse.cpu().numpy())
+
+
+def _run_caller(exe, mode, d):
+    print(f"[c-abi] {mode}", flush=True)
+    r = subprocess.run([exe, mode, str(d)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, (mode, r.returncode, r.stderr)
+    return d
+
+
+def _same(d, o, lse, o_shape, lse_shape):
+    o_c = np.frombuffer((d / "o.bin").read_bytes(), dtype=np.int16).reshape(o_shape)
+    l_c = np.frombuffer((d / "lse.bin").read_bytes(), dtype=np.float32).reshape(lse_shape)
+    assert np.array_equal(o_c, o.cpu().view(torch.int16).numpy())
+    assert np.array_equal(l_c, lse.cpu().numpy())
+
+
+@pytest.mark.gpu
+def test_c_caller_covers_the_other_entry_points(tmp_path):
+    """Packed forward, fp8, paged and standard-head decode from C, bit for bit the binding's result."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    mx.load_library()
+    exe = _build_caller(tmp_path)
+    dev = torch.device("cuda:0")
+
+    # Packed forward: GQA, causal + window, an empty segment, ragged tiles.
+    lq, lk, hq, hkv, d = [300, 0, 129], [333, 40, 129], 4, 2, 128
+    p = workloads.make_problem(7402, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=lq, lens_k=lk)
+    vd = tmp_path / "varlen"
+    vd.mkdir()
+    for x in "qkv":
+        _save(vd, f"{x}.bin", p[x])
+    _save(vd, "cu_q.bin", p["cu_seqlens_q"])
+    _save(vd, "cu_k.bin", p["cu_seqlens_k"])
+    scale = d ** -0.5
+    tq, tk = sum(lq), sum(lk)
+    (vd / "args.txt").write_text(f"{len(lq)} {max(lq)} {max(lk)} {tq} {tk} {hq} {hkv} {d} 1 100 0 0.0 {scale!r} 0\n")
+    _run_caller(exe, "varlen", vd)
+    o, lse = mx.mxfa_fwd_varlen(p["q"].to(dev), p["k"].to(dev), p["v"].to(dev), p["cu_seqlens_q"].to(dev),
+                                p["cu_seqlens_k"].to(dev), max(lq), max(lk), causal=True, window=(100, 0),
+                                scale=scale)
+    torch.cuda.synchronize()
+    _same(vd, o, lse, (tq, hq, d), (hq, tq))
+
+    # Standard-head decode, three splits.
+    lq, lk, hq, hkv, d, splits = [1, 2, 1], [700, 64, 300], 16, 2, 128, 3
+    p = workloads.make_problem(7403, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=lq, lens_k=lk)
+    gd = tmp_path / "gqa"
+    gd.mkdir()
+    for x in "qkv":
+        _save(gd, f"{x}.bin", p[x])
+    _save(gd, "cu_q.bin", p["cu_seqlens_q"])
+    _save(gd, "cu_k.bin", p["cu_seqlens_k"])
+    scale = d ** -0.5
+    tq, tk = sum(lq), sum(lk)
+    (gd / "args.txt").write_text(f"{len(lq)} {max(lq)} {max(lk)} {tq} {tk} {hq} {hkv} {d} 1 -1 -1 0.0 {scale!r} "
+                                 f"{splits}\n")
+    _run_caller(exe, "gqa", gd)
+    o, lse = mx.mxfa_decode_splitkv_gqa(p["q"].to(dev), p["k"].to(dev), p["v"].to(dev), p["cu_seqlens_q"].to(dev),
+                                        p["cu_seqlens_k"].to(dev), max(lq), max(lk), causal=True, scale=scale,
+                                        num_splits=splits)
+    torch.cuda.synchronize()
+    _same(gd, o, lse, (tq, hq, d), (hq, tq))
+
+    # Latent decode over an fp8 cache, two splits.
+    lq, lk, hq, hkv, splits = [4, 1], [500, 77], 16, 1, 2
+    p = workloads.make_problem(7404, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    p.update(workloads.quantize_e4m3(p["kv"].float()))
+    fd = tmp_path / "fp8"
+    fd.mkdir()
+    _save(fd, "q.bin", p["q"])
+    _save(fd, "kv.bin", p["kv8"].view(torch.uint8))
+    _save(fd, "cu_q.bin", p["cu_seqlens_q"])
+    _save(fd, "cu_k.bin", p["cu_seqlens_k"])
+    scale = 1.0 / math.sqrt(576)
+    tq, tk = sum(lq), sum(lk)
+    kv_scale = float(p["kv_scale"])
+    (fd / "args.txt").write_text(f"{len(lq)} {max(lq)} {max(lk)} {tq} {tk} {hq} {hkv} 0 -1 -1 0.0 {scale!r} "
+                                 f"{splits} {kv_scale!r}\n")
+    _run_caller(exe, "fp8", fd)
+    o, lse = mx.mxfa_decode_splitkv_fp8(p["q"].to(dev), p["kv8"].to(dev), p["cu_seqlens_q"].to(dev),
+                                        p["cu_seqlens_k"].to(dev), max(lq), max(lk), kv_scale, scale=scale,
+                                        num_splits=splits)
+    torch.cuda.synchronize()
+    _same(fd, o, lse, (tq, hq, 512), (hq, tq))
+
+    # Latent decode over a paged cache (64-row pages at shuffled indices).
+    lq, lk, hq, hkv, splits, page = [4, 2], [300, 130], 16, 1, 2, 64
+    p = workloads.make_problem(7405, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    pg = workloads.paginate(p["kv"], lk, page, torch.Generator("cpu").manual_seed(7406))
+    pd = tmp_path / "paged"
+    pd.mkdir()
+    _save(pd, "q.bin", p["q"])
+    _save(pd, "kv.bin", pg["kv_cache"])
+    _save(pd, "cu_q.bin", p["cu_seqlens_q"])
+    _save(pd, "seqlens.bin", pg["cache_seqlens"])
+    _save(pd, "table.bin", pg["block_table"])
+    tq = sum(lq)
+    num_pages, max_pages = pg["kv_cache"].shape[0], pg["block_table"].shape[1]
+    (pd / "args.txt").write_text(f"{len(lq)} {max(lq)} {max(lk)} {tq} {num_pages} {page} {max_pages} {hq} {hkv} "
+                                 f"0 -1 -1 0.0 {scale!r} {splits}\n")
+    _run_caller(exe, "paged", pd)
+    o, lse = mx.mxfa_decode_splitkv_paged(p["q"].to(dev), pg["kv_cache"].to(dev), p["cu_seqlens_q"].to(dev),
+                                          pg["cache_seqlens"].to(dev), pg["block_table"].to(dev), max(lq), max(lk),
+                                          scale=scale, num_splits=splits)
+    torch.cuda.synchronize()
+    _same(pd, o, lse, (tq, hq, 512), (hq, tq))

@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import workloads
-from tests.gpu_helpers import compare, dev, gpu_varlen, oracle_varlen, sample_rows, to_np
+from tests.gpu_helpers import Stats, compare, dev, gpu_varlen, oracle_varlen, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -95,6 +95,77 @@ def test_varlen_matches_oracle(case):
     o_g, lse_g = gpu_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
     o_ref, lse_ref, _ = oracle_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
     compare(o_g.reshape(-1, d), lse_g.T.reshape(-1), o_ref.reshape(-1, d), lse_ref.reshape(-1), dtype, str(case))
+
+
+def test_varlen_work_list_many_segments_dirty_workspace():
+    """The work list: more segments than one pass of its scan (1500), empty q and k
+    segments, a workspace full of garbage beforehand, then a smaller problem in the
+    same workspace -- every row against the oracle."""
+    rng = np.random.RandomState(2600)
+    for rep, batch in enumerate((1500, 37)):
+        lq = [int(x) for x in rng.randint(0, 70, batch)]
+        lk = [int(q + rng.randint(-5, 40)) if q else int(rng.randint(0, 3)) for q in lq]
+        lk = [max(0, x) for x in lk]
+        p = workloads.make_problem(2600 + rep, dtype="bf16", heads_q=4, heads_kv=2, d_qk=64, d_v=64, lens_q=lq,
+                                   lens_k=lk)
+        d = dev()
+        if rep == 0:
+            nbytes = mx.mxfa_fwd_varlen_workspace_bytes(batch, max(lq), 4, 64)
+            ws = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device=d)
+        print(f"[varlen] work list: {batch} segments, round {rep}", flush=True)
+        o, lse = mx.mxfa_fwd_varlen(p["q"].to(d), p["k"].to(d), p["v"].to(d), p["cu_seqlens_q"].to(d),
+                                    p["cu_seqlens_k"].to(d), max(lq), max(lk), causal=True, window=(20, 0),
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref, _ = oracle_varlen(p, causal=True, window=(20, 0), softcap=0.0, scale=64 ** -0.5)
+        compare(o.float().cpu().numpy().reshape(-1, 64), lse.cpu().numpy().T.reshape(-1), o_ref.reshape(-1, 64),
+                lse_ref.reshape(-1), "bf16", f"work list {batch} segments")
+
+
+# The prefill kernel has a variant of its own for scale <= 0 (the logits are
+# formed explicitly before the row max instead of folding the scale into the
+# exponent): dense and packed, d 64 and 128, causal, windowed and capped.
+NONPOS_CASES = [
+    (scale_mul, d, causal, window, cap, packed)
+    for scale_mul in (-1.0, 0.0)
+    for d, causal, window, cap, packed in [
+        (64, True, (-1, -1), 0.0, False),
+        (128, True, (-1, -1), 0.0, False),
+        (128, True, (70, 0), 0.0, True),
+        (64, False, (33, 20), 0.0, True),
+        (128, True, (-1, -1), 30.0, False),
+    ]
+]
+
+
+@pytest.mark.parametrize("case", NONPOS_CASES, ids=[
+    f"scale{c[0]:g}-d{c[1]}-c{int(c[2])}-w{c[3][0]},{c[3][1]}-cap{c[4]:g}-{'packed' if c[5] else 'dense'}"
+    for c in NONPOS_CASES])
+def test_prefill_nonpositive_scale(case):
+    scale_mul, d, causal, window, cap, packed = case
+    seed = 2500 + NONPOS_CASES.index(case)
+    scale = scale_mul * d ** -0.5
+    print(f"[prefill] scale={scale} case={case} seed={seed}", flush=True)
+    if packed:
+        lq, lk = [150, 0, 300], [200, 40, 300]
+        p = workloads.make_problem(seed, dtype="bf16", heads_q=4, heads_kv=2, d_qk=d, d_v=d, lens_q=lq, lens_k=lk)
+        o_g, lse_g = gpu_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
+        o_ref, lse_ref, _ = oracle_varlen(p, causal=causal, window=window, softcap=cap, scale=scale)
+        compare(o_g.reshape(-1, d), lse_g.T.reshape(-1), o_ref.reshape(-1, d), lse_ref.reshape(-1), "bf16",
+                str(case))
+        return
+    b, sq, sk, hq, hkv = 2, 261, 261, 4, 2
+    p = workloads.make_problem(seed, dtype="bf16", heads_q=hq, heads_kv=hkv, d_qk=d, d_v=d, lens_q=[sq] * b,
+                               lens_k=[sk] * b, dense=True)
+    q, k, v = p["q"].to(dev()), p["k"].to(dev()), p["v"].to(dev())
+    o, lse = mx.mxfa_fwd(q, k, v, causal=causal, window=window, softcap=cap, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, _ = oracle_varlen(
+        {"q": p["q"].reshape(b * sq, hq, d), "k": p["k"].reshape(b * sk, hkv, d),
+         "v": p["v"].reshape(b * sk, hkv, d), "cu_seqlens_q": p["cu_seqlens_q"], "cu_seqlens_k": p["cu_seqlens_k"]},
+        causal=causal, window=window, softcap=cap, scale=scale)
+    compare(o.float().cpu().numpy().reshape(-1, d), lse.cpu().numpy().transpose(0, 2, 1).reshape(-1),
+            o_ref.reshape(-1, d), lse_ref.reshape(-1), "bf16", str(case))
 
 
 def test_zero_length_calls_are_noops():
@@ -492,7 +563,27 @@ def test_gqa_decode_independent_of_split_count():
 
 # --------------------------------------------------- headline workloads, full size
 
-def _full_dense_or_varlen(name, n_rows):
+def _oracle_all_rows(label, dtype, o_c, lse_c, run_rows, total_tokens, heads, chunk_tokens):
+    """Compare every (token, head) row of a GPU result with the oracle, a chunk of tokens at a time.
+
+    o_c [T, H, d_v] and lse_c [T, H] are the GPU outputs (token-major); run_rows(rows) returns the
+    oracle's (O, LSE) for an int array of (token, head) rows.
+    """
+    st = Stats(dtype, label)
+    for t0 in range(0, total_tokens, chunk_tokens):
+        t1 = min(total_tokens, t0 + chunk_tokens)
+        tok = np.repeat(np.arange(t0, t1, dtype=np.int64), heads)
+        head = np.tile(np.arange(heads, dtype=np.int64), t1 - t0)
+        rows = np.stack([tok, head], axis=1)
+        o_ref, lse_ref = run_rows(rows)
+        st.add(o_c[t0:t1].reshape(-1, o_c.shape[-1]), lse_c[t0:t1].reshape(-1), o_ref, lse_ref)
+        print(f"[full] {label}: tokens {t0}..{t1 - 1} of {total_tokens}: max|dO| so far {st.max_o:.4g}, "
+              f"max|dLSE| {st.max_l:.3g}", flush=True)
+    return st.check()
+
+
+def _full_dense_or_varlen(name, chunk_tokens):
+    """The whole workload on the GPU in the launch configuration the bench times; every row against the oracle."""
     w = workloads.get(name)
     print(f"[full] {name}: generating inputs", flush=True)
     inp = workloads.make_inputs(w)
@@ -515,19 +606,21 @@ def _full_dense_or_varlen(name, n_rows):
         torch.cuda.synchronize()
         lse = lse.T
         qn, kn, vn = inp["q"], inp["k"], inp["v"]
-    rows = sample_rows(inp["lens_q"], w.heads_q, n_rows, seed=w.seed)
-    print(f"[full] {name}: oracle on {len(rows)} rows", flush=True)
     import oracle
 
-    o_ref, lse_ref, _ = oracle.attention_rows(to_np(qn), to_np(kn), to_np(vn), inp["cu_seqlens_q"].numpy(),
-                                              inp["cu_seqlens_k"].numpy(), causal=w.causal, window=w.window,
-                                              softcap=w.softcap, scale=scale, rows=rows)
     o_c = o.float().cpu().numpy()
     lse_c = lse.cpu().numpy()
+    del o, lse, q, k, v
     assert np.all(np.isfinite(lse_c)), "every row of these workloads sees at least one key"
-    got_o = o_c[rows[:, 0], rows[:, 1]]
-    got_l = lse_c[rows[:, 0], rows[:, 1]]
-    return compare(got_o, got_l, o_ref, lse_ref, w.dtype, name)
+    qn, kn, vn = to_np(qn), to_np(kn), to_np(vn)
+    cq, ck = inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy()
+
+    def run_rows(rows):
+        o_ref, lse_ref, _ = oracle.attention_rows(qn, kn, vn, cq, ck, causal=w.causal, window=w.window,
+                                                  softcap=w.softcap, scale=scale, rows=rows)
+        return o_ref, lse_ref
+
+    return _oracle_all_rows(name, w.dtype, o_c, lse_c, run_rows, o_c.shape[0], w.heads_q, chunk_tokens)
 
 
 def test_full_single_head_f32():
@@ -544,21 +637,28 @@ def test_full_single_head_f32():
             o_ref.reshape(-1, 64), lse_ref.transpose(0, 2, 1).reshape(-1), "f32", "single_head_f32")
 
 
+# Every row of each full-size workload is compared. The oracle takes about
+# 2.5 s (causal prefill), 19 s (varlen), 75 s (window + softcap) and 40 s
+# (chunked prefill) on 16 host cores.
+@pytest.mark.timeout(600)
 def test_full_causal_prefill_bf16():
-    _full_dense_or_varlen("causal_prefill_bf16", 512)
+    _full_dense_or_varlen("causal_prefill_bf16", 2048)
 
 
+@pytest.mark.timeout(600)
 def test_full_varlen_gqa_causal_bf16():
-    _full_dense_or_varlen("varlen_gqa_causal_bf16", 512)
+    _full_dense_or_varlen("varlen_gqa_causal_bf16", 4096)
 
 
+@pytest.mark.timeout(900)
 def test_full_window_softcap_bf16():
-    _full_dense_or_varlen("window_softcap_bf16", 384)
+    _full_dense_or_varlen("window_softcap_bf16", 4096)
 
 
+@pytest.mark.timeout(900)
 def test_full_chunked_prefill_bf16():
     # Sq < Sk: the chunk's rows see the whole cached prefix plus their causal part.
-    _full_dense_or_varlen("chunked_prefill_bf16", 384)
+    _full_dense_or_varlen("chunked_prefill_bf16", 512)
 
 
 def test_decode_long_context():
@@ -636,6 +736,7 @@ def test_prefill_after_kernels_that_leave_other_data_in_lds():
             assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
 
 
+@pytest.mark.timeout(600)
 def test_full_mla_decode_bf16():
     w = workloads.get("mla_decode_bf16")
     print("[full] mla_decode_bf16: generating inputs", flush=True)
@@ -645,15 +746,21 @@ def test_full_mla_decode_bf16():
     o, lse = mx.mxfa_decode_splitkv(q, kv, inp["cu_seqlens_q"].to(d), inp["cu_seqlens_k"].to(d), w.seqlen_q,
                                     w.seqlen_k, head_dim_v=w.d_v, scale=w.softmax_scale)
     torch.cuda.synchronize()
-    rows = sample_rows(inp["lens_q"], w.heads_q, 256, seed=w.seed)
-    import oracle
-
-    kvn = to_np(inp["kv"])
-    o_ref, lse_ref, _ = oracle.attention_rows(to_np(inp["q"]), kvn, kvn[:, :, :w.d_v], inp["cu_seqlens_q"].numpy(),
-                                              inp["cu_seqlens_k"].numpy(), scale=w.softmax_scale, rows=rows)
     o_c = o.float().cpu().numpy()
     lse_c = lse.T.cpu().numpy()
-    compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "mla_decode_bf16")
+    del q, kv, o, lse
+    import oracle
+
+    qn, kvn = to_np(inp["q"]), to_np(inp["kv"])
+    cq, ck = inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy()
+
+    def run_rows(rows):
+        o_ref, lse_ref, _ = oracle.attention_rows(qn, kvn, kvn[:, :, :w.d_v], cq, ck, scale=w.softmax_scale,
+                                                  rows=rows)
+        return o_ref, lse_ref
+
+    # Every one of the 512 x 16 rows.
+    _oracle_all_rows("mla_decode_bf16", "bf16", o_c, lse_c, run_rows, o_c.shape[0], w.heads_q, 128)
 
 
 def test_full_paged_mla_decode_bf16():
@@ -713,6 +820,7 @@ def test_full_gqa_decode_bf16():
             lse_ref.reshape(-1), "bf16", "gqa_decode_bf16")
 
 
+@pytest.mark.timeout(600)
 def test_full_mla_decode_fp8():
     w = workloads.get("mla_decode_fp8")
     print("[full] mla_decode_fp8: generating inputs", flush=True)
@@ -722,12 +830,18 @@ def test_full_mla_decode_fp8():
                                         inp["cu_seqlens_k"].to(d), w.seqlen_q, w.seqlen_k, inp["kv_scale"],
                                         head_dim_v=w.d_v, scale=w.softmax_scale)
     torch.cuda.synchronize()
-    rows = sample_rows(inp["lens_q"], w.heads_q, 256, seed=w.seed)
-    import oracle
-
-    o_ref, lse_ref, _ = oracle.attention_rows_fp8_latent(to_np(inp["q"]), inp["kv8"].numpy(), inp["kv_scale"],
-                                                         inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy(),
-                                                         d_v=w.d_v, scale=w.softmax_scale, rows=rows)
     o_c = o.float().cpu().numpy()
     lse_c = lse.T.cpu().numpy()
-    compare(o_c[rows[:, 0], rows[:, 1]], lse_c[rows[:, 0], rows[:, 1]], o_ref, lse_ref, "bf16", "mla_decode_fp8")
+    del o, lse
+    import oracle
+
+    qn, kv8 = to_np(inp["q"]), inp["kv8"].numpy()
+    cq, ck = inp["cu_seqlens_q"].numpy(), inp["cu_seqlens_k"].numpy()
+
+    def run_rows(rows):
+        o_ref, lse_ref, _ = oracle.attention_rows_fp8_latent(qn, kv8, inp["kv_scale"], cq, ck, d_v=w.d_v,
+                                                             scale=w.softmax_scale, rows=rows)
+        return o_ref, lse_ref
+
+    # Every one of the 512 x 16 rows, in one oracle call (the cache is dequantised once per call).
+    _oracle_all_rows("mla_decode_fp8", "bf16", o_c, lse_c, run_rows, o_c.shape[0], w.heads_q, o_c.shape[0])

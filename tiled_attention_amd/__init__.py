@@ -21,6 +21,7 @@ __all__ = [
     "load_library",
     "mxfa_fwd",
     "mxfa_fwd_varlen",
+    "mxfa_fwd_varlen_workspace_bytes",
     "mxfa_decode_splitkv",
     "mxfa_decode_splitkv_paged",
     "mxfa_decode_splitkv_fp8",
@@ -45,7 +46,8 @@ _c_int, _c_float, _vp, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctyp
 # C signatures of include/mxfa.h.
 _SIGNATURES = {
     "mxfa_fwd": (_c_int, [_vp] * 5 + [_c_int] * 10 + [_c_float, _c_float, _vp]),
-    "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp]),
+    "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp, _sz, _vp]),
+    "mxfa_fwd_varlen_workspace_bytes": (_sz, [_c_int] * 4),
     "mxfa_decode_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_paged": (_c_int, [_vp] * 7 + [_c_int] * 14 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_fp8": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float] * 3 + [_c_int, _vp, _sz, _vp]),
@@ -162,11 +164,18 @@ def mxfa_fwd(q, k, v, *, causal=False, window=(-1, -1), softcap=0.0, scale=None,
     return out, lse
 
 
+def mxfa_fwd_varlen_workspace_bytes(batch, max_seqlen_q, heads_q, head_dim) -> int:
+    return int(load_library().mxfa_fwd_varlen_workspace_bytes(batch, max_seqlen_q, heads_q, head_dim))
+
+
 def mxfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
-                    window=(-1, -1), softcap=0.0, scale=None, out=None, lse=None, return_lse=True):
+                    window=(-1, -1), softcap=0.0, scale=None, workspace=None, out=None, lse=None,
+                    return_lse=True):
     """Packed forward: q [Tq,Hq,d], k/v [Tk,Hkv,d], int32 cu_seqlens [B+1] on the GPU.
 
-    Returns (o [Tq,Hq,d], lse [Hq,Tq] fp32).
+    Returns (o [Tq,Hq,d], lse [Hq,Tq] fp32). ``workspace`` is a uint8 GPU
+    tensor of at least mxfa_fwd_varlen_workspace_bytes() bytes for the work
+    list (allocated here when None).
     """
     lib = load_library()
     _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [T, H, d]")
@@ -183,12 +192,16 @@ def mxfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
         lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _need(lse is None or (lse.shape == (hq, tq) and lse.dtype == torch.float32), "lse must be [Hq,Tq] fp32")
-    dev = _tensors_ok(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
+    dev = _tensors_ok(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, workspace)
     with torch.cuda.device(dev):
+        if workspace is None:
+            nbytes = mxfa_fwd_varlen_workspace_bytes(batch, int(max_seqlen_q), hq, d)
+            workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
         st = lib.mxfa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
                                  _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), tq, tk, hq,
                                  hkv, d, _dtype_code(q), int(bool(causal)), int(window[0]), int(window[1]),
-                                 float(softcap), _scale(scale, d), _stream(dev))
+                                 float(softcap), _scale(scale, d), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(dev))
     _check(st)
     return out, lse
 

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
     __shared__ __attribute__((aligned(TILEB))) char sK1[TILEB];
     __shared__ __attribute__((aligned(TILEB))) char sV0[TILEB];
     __shared__ __attribute__((aligned(TILEB))) char sV1[TILEB];
-    __shared__ float sML[2][2][ROWS];  // per wave: row max, row sum
+    __shared__ float sML[2][3][ROWS];  // per wave: row max, row sum (fp32), row sum of the bf16 weights
 
     int id = blockIdx.x;
     const int sp = id % p.splits;
@@ -188,7 +188,8 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) acc[db] = f32x16_t{};
     float m_run = -INFINITY;  // running max of this row, log2 units (may trail the true max by <= 8)
-    float l_part = 0.0f;      // running sum over this lane's keys
+    float l_part = 0.0f;      // running sum of p over this lane's keys (fp32; for the LSE)
+    float lb_part = 0.0f;     // running sum of bf16(p), the weights the P V MFMAs use (normalises O)
 
     // One tile: scores, softmax, P V for this wave's 32 keys.
     auto tile_step = [&](const char* sK, const char* sV, int kt) __attribute__((always_inline)) {
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
             const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
             m_run = m_new;
             l_part *= alpha;
+            lb_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
         }
@@ -228,6 +230,7 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
             const float p1 = fast_exp2(s[r + 1] + nb);
             psum += p0 + p1;
             pk[r >> 1] = pack_bf16x2(p0, p1);
+            lb_part = add_bf16x2(pk[r >> 1], lb_part);
         }
         l_part += psum;
         uint32_t vxl[2] = {vx[0], vx[1]};
@@ -284,18 +287,23 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // Merge the two waves: M = max of the waves' maxima, each accumulator
-    // scaled by exp2(m_w - M), L = sum of the scaled row sums.
+    // scaled by exp2(m_w - M), L (fp32 sums) and Lb (sums of the bf16
+    // weights) the scaled row sums.
     const float l_row = half_sum(l_part);
+    const float lb_row = half_sum(lb_part);
     if (lh == 0) {
         sML[w][0][lr] = m_run;
         sML[w][1][lr] = l_row;
+        sML[w][2][lr] = lb_row;
     }
     lds_barrier();
     const float m0 = sML[0][0][lr], m1 = sML[1][0][lr];
     const float M = fmaxf(m0, m1);
-    float L = 0.0f, f_mine = 0.0f;
+    float L = 0.0f, Lb = 0.0f, f_mine = 0.0f;
     if (M != -INFINITY) {
-        L = sML[0][1][lr] * fast_exp2(m0 - M) + sML[1][1][lr] * fast_exp2(m1 - M);
+        const float f0 = fast_exp2(m0 - M), f1 = fast_exp2(m1 - M);
+        L = sML[0][1][lr] * f0 + sML[1][1][lr] * f1;
+        Lb = sML[0][2][lr] * f0 + sML[1][2][lr] * f1;
         f_mine = fast_exp2(m_run - M);
     }
     f32x4_t* const xbuf = reinterpret_cast<f32x4_t*>(sK0);  // [DBLK][4][64] float4
@@ -320,7 +328,8 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
 
     // Lane lr holds row my_row, channels 32*db + 8*q4 + 4*lh .. +3.
     if (p.splits == 1) {
-        const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+        // O over the sum of the bf16 weights the P V MFMAs used; the LSE from the fp32 sum.
+        const float inv = (Lb > 0.0f) ? 1.0f / Lb : 0.0f;
         uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + my_tok) * p.heads_q + my_head) * D + 4 * lh;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
@@ -343,15 +352,16 @@ __global__ __launch_bounds__(NT) void decode_gqa_split_kernel(const GqaDecodePar
             *reinterpret_cast<f32x4_t*>(pacc + 32 * db + 8 * q4) =
                 f32x4_t{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
     if (lh == 0) {
-        float* pml = p.part_ml + pidx * 2 * ROWS;
+        float* pml = p.part_ml + pidx * 3 * ROWS;
         pml[lr] = M;
         pml[ROWS + lr] = L;
+        pml[2 * ROWS + lr] = Lb;
     }
 }
 
 // Merge the splits of one (sequence, kv head, row group): M = max_s m_s,
-// w_s = exp2(m_s - M), O = sum_s w_s acc_s / sum_s w_s l_s,
-// LSE = ln2 * (M + log2 sum_s w_s l_s). One thread per (row, 4 channels).
+// w_s = exp2(m_s - M), O = sum_s w_s acc_s / sum_s w_s lb_s (lb: sums of the
+// bf16 weights), LSE = ln2 * (M + log2 sum_s w_s l_s) (l: fp32 sums). One thread per (row, 4 channels).
 // The splits are read in chunks of 8 whose loads are all issued before any
 // is used (one memory round trip per chunk), merged with a running max.
 constexpr int kCombineThreads = 64;  // small groups spread the few valid rows over many CUs
@@ -378,17 +388,18 @@ __global__ __launch_bounds__(kCombineThreads) void decode_gqa_combine_kernel(con
     const int tok = r / G;
     const int h = g * G + r % G;
     const long long pidx0 = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits;
-    float M = -INFINITY, L = 0.0f;
+    float M = -INFINITY, L = 0.0f, Lb = 0.0f;
     f32x4_t o = f32x4_t{};
     for (int s0 = 0; s0 < p.splits; s0 += CH) {
-        float ms[CH], ls[CH];
+        float ms[CH], ls[CH], lbs[CH];
         f32x4_t as[CH];
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const bool in = s0 + j < p.splits;
             const long long pi = pidx0 + (in ? s0 + j : 0);
-            ms[j] = in ? p.part_ml[pi * 2 * ROWS + row] : -INFINITY;
-            ls[j] = p.part_ml[pi * 2 * ROWS + ROWS + row];
+            ms[j] = in ? p.part_ml[pi * 3 * ROWS + row] : -INFINITY;
+            ls[j] = p.part_ml[pi * 3 * ROWS + ROWS + row];
+            lbs[j] = p.part_ml[pi * 3 * ROWS + 2 * ROWS + row];
             as[j] = *reinterpret_cast<const f32x4_t*>(p.part_acc + (pi * ROWS + row) * D + d0);
         }
         float mc = M;
@@ -397,16 +408,18 @@ __global__ __launch_bounds__(kCombineThreads) void decode_gqa_combine_kernel(con
         if (mc == -INFINITY) continue;  // nothing visible so far
         const float a = fast_exp2(M - mc);  // 0 while M is -inf
         L *= a;
+        Lb *= a;
         o *= a;
 #pragma unroll
         for (int j = 0; j < CH; ++j) {
             const float ws = fast_exp2(ms[j] - mc);  // 0 for splits past the end or with no keys
             L += ws * ls[j];
+            Lb += ws * lbs[j];
             o += ws * as[j];
         }
         M = mc;
     }
-    const float inv = (L > 0.0f) ? 1.0f / L : 0.0f;
+    const float inv = (Lb > 0.0f) ? 1.0f / Lb : 0.0f;
     uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * D + d0;
     store_u32x2(O, u32x2_t{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)});
     if (p.lse && d0 == 0)

@@ -279,7 +279,8 @@ void decode_split_kernel(const DecodeParams p) {
 #pragma unroll
     for (int cb = 0; cb < CBLK; ++cb) acc[cb] = f32x16_t{};
     float m_run = -INFINITY;  // running max of row my_row, log2 units (may trail the true max by <= 8)
-    float l_part = 0.0f;      // running sum over this lane's keys
+    float l_part = 0.0f;      // running sum of p over this lane's keys (fp32; for the LSE)
+    float lb_part = 0.0f;     // running sum of bf16(p), the weights the P V MFMAs use (normalises O)
 
     // Partial S^T over this wave's channel half.
     auto qk_tile = [&](const char* tile) __attribute__((always_inline)) -> f32x16_t {
@@ -341,6 +342,7 @@ void decode_split_kernel(const DecodeParams p) {
         // the tile's own max only when some lane's sum of P exceeds 2^8.
         const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
         float psum = 0.0f;
+        float psb = 0.0f;
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -365,6 +367,7 @@ void decode_split_kernel(const DecodeParams p) {
                 const float p1 = fast_exp2(x[r + 1] + nb);
                 psum += p0 + p1;
                 pk[r >> 1] = pack_bf16x2(p0, p1);
+                psb = add_bf16x2(pk[r >> 1], psb);
             }
             if (ks == 6) mid_hook();
             __builtin_amdgcn_sched_barrier(0);
@@ -380,15 +383,18 @@ void decode_split_kernel(const DecodeParams p) {
             m_run = m_new;
             const float nb2 = (m_run == -INFINITY) ? 0.0f : -m_run;
             psum = 0.0f;
+            psb = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 const float p0 = fast_exp2(x[r] + nb2);
                 const float p1 = fast_exp2(x[r + 1] + nb2);
                 psum += p0 + p1;
                 pk[r >> 1] = pack_bf16x2(p0, p1);
+                psb = add_bf16x2(pk[r >> 1], psb);
             }
         }
         l_part = l_part * alpha + psum;
+        lb_part = lb_part * alpha + psb;
         return sn;
     };
     // O^T += V^T P^T over the tile's two 16-key steps.
@@ -558,6 +564,7 @@ void decode_split_kernel(const DecodeParams p) {
     // 256*ch + 32*cb + 8*(r/4) + 4*lh + r%4.
     const long long pidx = (((long long)b * p.heads_kv + g) * p.m_groups + mg) * p.splits + sp;
     const float l_row = half_sum(l_part);
+    const float lb_row = half_sum(lb_part);
     const int grow_idx = 32 * rb + lr;
     float* pacc = p.part_acc + (pidx * ROWS + grow_idx) * DV + 256 * ch + 4 * lh;
 #pragma unroll
@@ -567,14 +574,16 @@ void decode_split_kernel(const DecodeParams p) {
             *reinterpret_cast<f32x4_t*>(pacc + 32 * cb + 8 * q4) =
                 f32x4_t{acc[cb][4 * q4], acc[cb][4 * q4 + 1], acc[cb][4 * q4 + 2], acc[cb][4 * q4 + 3]};
     if (ch == 0 && lh == 0) {
-        float* pml = p.part_ml + pidx * 2 * ROWS;
+        float* pml = p.part_ml + pidx * 3 * ROWS;
         pml[grow_idx] = m_run;
         pml[ROWS + grow_idx] = l_row;
+        pml[2 * ROWS + grow_idx] = lb_row;
     }
 }
 
 // Merge the splits: M = max_s m_s, w_s = exp2(m_s - M),
-// O = sum_s w_s acc_s / sum_s w_s l_s, LSE = ln2 * (M + log2 sum_s w_s l_s),
+// O = sum_s w_s acc_s / sum_s w_s lb_s (lb: sums of the bf16 weights the P V
+// MFMAs used), LSE = ln2 * (M + log2 sum_s w_s l_s) (l: fp32 sums),
 // with a running max over chunks of splits. One thread per (row, 16
 // channels); 8 rows per work group.
 constexpr int CROWS = NTHREADS / 32;
@@ -600,19 +609,20 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
     // One pass with a running max over chunks of CH splits; all loads of a
     // chunk are issued before any is used (one memory round trip per chunk).
     constexpr int CH = 2;
-    float M = -INFINITY, L = 0.0f;
+    float M = -INFINITY, L = 0.0f, Lb = 0.0f;
     float o[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[j] = 0.0f;
     for (int s0 = 0; s0 < p.splits; s0 += CH) {
-        float ms[CH], ls[CH];
+        float ms[CH], ls[CH], lbs[CH];
         f32x4_t as[CH][4];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const bool in = s0 + c < p.splits;
             const long long pi = pidx0 + (in ? s0 + c : 0);
-            ms[c] = in ? p.part_ml[pi * 2 * ROWS + row] : -INFINITY;
-            ls[c] = p.part_ml[pi * 2 * ROWS + ROWS + row];
+            ms[c] = in ? p.part_ml[pi * 3 * ROWS + row] : -INFINITY;
+            ls[c] = p.part_ml[pi * 3 * ROWS + ROWS + row];
+            lbs[c] = p.part_ml[pi * 3 * ROWS + 2 * ROWS + row];
             const f32x4_t* a = reinterpret_cast<const f32x4_t*>(p.part_acc + (pi * ROWS + row) * DV + d0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) as[c][j] = a[j];
@@ -623,12 +633,14 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
         if (mc == -INFINITY) continue;  // nothing visible so far
         const float rs = fast_exp2(M - mc);  // 0 while M is -inf
         L *= rs;
+        Lb *= rs;
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[j] *= rs;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const float ws = fast_exp2(ms[c] - mc);  // 0 for splits past the end or with no keys
             L += ws * ls[c];
+            Lb += ws * lbs[c];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 o[4 * j + 0] += ws * as[c][j][0];
@@ -639,7 +651,7 @@ __global__ __launch_bounds__(NTHREADS) void decode_combine_kernel(const DecodePa
         }
         M = mc;
     }
-    const float inv = (L > 0.0f) ? p.v_scale / L : 0.0f;  // v_scale: the fp8 cache's dequantisation scale
+    const float inv = (Lb > 0.0f) ? p.v_scale / Lb : 0.0f;  // v_scale: the fp8 cache's dequantisation scale
     uint16_t* O = static_cast<uint16_t*>(p.o) + ((long long)(q_start + tok) * p.heads_q + h) * DV + d0;
     u32x4_t v0, v1;
 #pragma unroll

@@ -40,8 +40,8 @@
 namespace mxfa {
 namespace {
 
-constexpr int BM = 128;        // query rows per work group
-constexpr int BN = 64;         // keys per tile
+constexpr int BM = kFwdBf16Rows;  // 128 query rows per work group
+constexpr int BN = kFwdBf16Keys;  // 64 keys per tile
 constexpr int NTHREADS = 256;  // 4 waves
 constexpr float kLazyRescale = 8.0f;  // log2 units: rescale when a row max grows by > 2^8
 constexpr float kOptimisticSum = 256.0f;  // a tile's P sum (per lane) up to which no p can exceed 2^8
@@ -102,7 +102,9 @@ void fwd_bf16_kernel(const FwdParams p) {
     __shared__ __attribute__((aligned(TILEB))) char sV0[TILEB];
     __shared__ __attribute__((aligned(TILEB))) char sV1[TILEB];
 
-    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles, p.xcd_cus);
+    const WorkItem item = p.worklist
+                              ? map_listed(blockIdx.x, p.worklist, p.batch, p.heads_kv, p.group, p.list_max, p.xcd_cus)
+                              : map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles, p.xcd_cus);
     if (item.b < 0) return;
     const int b = item.b;
     const int h = item.h;
@@ -214,7 +216,8 @@ void fwd_bf16_kernel(const FwdParams p) {
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) acc[i] = f32x16_t{};
     float m_run = -INFINITY;  // running max of this row, log2 units (may trail the true max by <= 8)
-    float l_part = 0.0f;      // running sum over this lane's keys
+    float l_part = 0.0f;      // running sum of p over this lane's keys (fp32; for the LSE)
+    float lb_part = 0.0f;     // running sum of bf16(p), the weights the P V MFMAs use (normalises O)
     const float c_exp = (kMode == 0) ? p.x_mul : 1.0f;
 
     // ---- pipeline pieces
@@ -278,15 +281,18 @@ void fwd_bf16_kernel(const FwdParams p) {
             const float alpha = grow ? fast_exp2(m_run - m_new) : 1.0f;
             m_run = m_new;
             l_part *= alpha;
+            lb_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
         }
     };
     // P = exp2(logit - max) as bf16 pairs; P^T operand (kb, half) = registers
-    // 8*half..8*half+7 of S^T block kb.
-    auto exp_tile = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8]) {
+    // 8*half..8*half+7 of S^T block kb. Returns the fp32 sum of p; psb gets
+    // the sum of the rounded values.
+    auto exp_tile = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8], float& psb) {
         const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
         float psum = 0.0f;
+        psb = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -295,6 +301,7 @@ void fwd_bf16_kernel(const FwdParams p) {
                 const float p1 = fast_exp2(fmaf(s[kb][r + 1], c_exp, nb));
                 psum += p0 + p1;
                 pk[kb][r >> 1] = pack_bf16x2(p0, p1);
+                psb = add_bf16x2(pk[kb][r >> 1], psb);
             }
         }
         return psum;
@@ -304,7 +311,7 @@ void fwd_bf16_kernel(const FwdParams p) {
     // is <= 2^8 -- the bound the lazy rescale keeps -- and the tile is done
     // without its row max. Otherwise (the max grew, or no key was seen yet)
     // take the tile's max, rescale and recompute P.
-    auto settle = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8], float psum) __attribute__((always_inline)) {
+    auto settle = [&](f32x16_t (&s)[2], uint32_t (&pk)[2][8], float psum, float psb) __attribute__((always_inline)) {
         if (wave_any(m_run == -INFINITY || psum > kOptimisticSum)) {
             float mt = -INFINITY;
 #pragma unroll
@@ -317,11 +324,13 @@ void fwd_bf16_kernel(const FwdParams p) {
             const float alpha = (m_new == m_run) ? 1.0f : fast_exp2(m_run - m_new);
             m_run = m_new;
             l_part *= alpha;
+            lb_part *= alpha;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
-            psum = exp_tile(s, pk);
+            psum = exp_tile(s, pk, psb);
         }
         l_part += psum;
+        lb_part += psb;
     };
     // O^T += V^T P^T for one tile.
     auto pv = [&](const uint32_t (&pk)[2][8], const char* vt_lds) __attribute__((always_inline)) {
@@ -343,8 +352,8 @@ void fwd_bf16_kernel(const FwdParams p) {
     // ALU turns S_j into P_j. After each MFMA one slice of the exponentials
     // (two elements), fenced so that the compiler keeps the interleave; the K
     // operand reads run AHEAD MFMAs ahead.
-    auto qk_exp = [&](f32x16_t (&sn)[2], const char* kt_lds, f32x16_t (&sc)[2],
-                      uint32_t (&pk)[2][8]) __attribute__((always_inline)) {
+    auto qk_exp = [&](f32x16_t (&sn)[2], const char* kt_lds, f32x16_t (&sc)[2], uint32_t (&pk)[2][8],
+                      float& psb) __attribute__((always_inline)) {
         constexpr int NM = 2 * KSTEPS;  // MFMAs: m = 2*ks + kb
         constexpr int EPS = 32 / NM;    // exponentials per slice
         constexpr int AHEAD = 4;
@@ -361,6 +370,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         for (int m = 0; m < AHEAD; ++m) a[m] = rd(m);
         const float nb = (m_run == -INFINITY) ? 0.0f : -m_run;
         float psum = 0.0f;
+        psb = 0.0f;
         // Raised issue priority for this phase: where the two waves sharing a
         // SIMD (one from each work group) are both ready, the one in its
         // exponential phase goes first, and its vector work then fills the
@@ -381,6 +391,7 @@ void fwd_bf16_kernel(const FwdParams p) {
                 const float p1 = fast_exp2(fmaf(sc[kb][r + 1], c_exp, nb));
                 pk[kb][r >> 1] = pack_bf16x2(p0, p1);
                 psum += p0 + p1;
+                psb = add_bf16x2(pk[kb][r >> 1], psb);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -490,7 +501,9 @@ void fwd_bf16_kernel(const FwdParams p) {
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
-                settle(s_cur, pk, qk_exp(s_next, k_use, s_cur, pk));
+                float psb;
+                const float psum = qk_exp(s_next, k_use, s_cur, pk, psb);
+                settle(s_cur, pk, psum, psb);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
                 if (tile_full(kt + BN))
                     pv_mask(mask0{}, pk, v_use, s_next, kt + BN);
@@ -499,7 +512,9 @@ void fwd_bf16_kernel(const FwdParams p) {
                 else
                     pv_mask(mask2{}, pk, v_use, s_next, kt + BN);
             } else {
-                settle(s_cur, pk, exp_tile(s_cur, pk));
+                float psb;
+                const float psum = exp_tile(s_cur, pk, psb);
+                settle(s_cur, pk, psum, psb);
                 pv(pk, v_use);
             }
             wait_vmem();
@@ -521,10 +536,13 @@ void fwd_bf16_kernel(const FwdParams p) {
         }
     }
 
-    // Epilogue: combine the two lane halves' sums, normalise, store.
+    // Epilogue: combine the two lane halves' sums, normalise, store. O is
+    // divided by the sum of the bf16 weights the P V MFMAs multiplied (so
+    // the weights of a row sum to one), the LSE takes the fp32 sum.
     const float l_row = half_sum(l_part);
+    const float lb_row = half_sum(lb_part);
     if (!q_valid) return;
-    const float inv = (l_row > 0.0f) ? 1.0f / l_row : 0.0f;
+    const float inv = (lb_row > 0.0f) ? 1.0f / lb_row : 0.0f;
     uint16_t* O = static_cast<uint16_t*>(p.o) + (long long)(q_start + qi) * q_tok + (long long)h * D;
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) {
@@ -553,7 +571,8 @@ template <int D>
 hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     FwdParams p = args;
     p.n_qtiles = (p.seqlen_q + BM - 1) / BM;
-    const long long grid = workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
+    const long long grid = p.worklist ? listed_workgroup_count(p.heads_kv, p.group, p.list_max)
+                                      : workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)

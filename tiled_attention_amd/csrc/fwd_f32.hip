@@ -16,8 +16,9 @@ namespace {
 
 constexpr int NTHREADS = 256;
 constexpr int LPR = 8;                    // lanes per query row
-constexpr int BM = NTHREADS / LPR;        // 32 query rows per work group
-constexpr int BN = 32;                    // keys per tile
+constexpr int BM = kFwdF32Rows;           // 32 query rows per work group (NTHREADS / LPR)
+constexpr int BN = kFwdF32Keys;           // 32 keys per tile
+static_assert(BM == NTHREADS / LPR, "one row per LPR lanes");
 
 template <int D, bool kCap>
 __global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
@@ -25,7 +26,8 @@ __global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
     __shared__ __attribute__((aligned(16))) float sK[BN * RS];
     __shared__ __attribute__((aligned(16))) float sV[BN * RS];
 
-    const WorkItem item = map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
+    const WorkItem item = p.worklist ? map_listed(blockIdx.x, p.worklist, p.batch, p.heads_kv, p.group, p.list_max)
+                                     : map_workgroup(blockIdx.x, p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (item.b < 0) return;
     const int b = item.b;
     const int h = item.h;
@@ -184,7 +186,8 @@ template <int D>
 hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     FwdParams p = args;
     p.n_qtiles = (p.seqlen_q + BM - 1) / BM;
-    const long long grid = workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
+    const long long grid = p.worklist ? listed_workgroup_count(p.heads_kv, p.group, p.list_max)
+                                      : workgroup_count(p.batch, p.heads_kv, p.group, p.n_qtiles);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)

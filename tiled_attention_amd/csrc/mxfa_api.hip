@@ -64,6 +64,22 @@ void fill_scaling(float scale, float softcap, float* x_mul, float* cap_mul, floa
 
 int device_cus(int* out);
 
+// Work-list length bound of a packed forward with bm-row q tiles: no more
+// than batch * ceil(max_seqlen_q / bm), nor ceil(total_q / bm) + batch.
+long long varlen_list_max(int batch, int max_seqlen_q, int total_q, int bm) {
+    const long long a = (long long)batch * ((max_seqlen_q + bm - 1) / bm);
+    const long long b = ((long long)total_q + bm - 1) / bm + batch;
+    return a < b ? a : b;
+}
+
+// Workspace bytes the size query promises: the list for the smallest q tile
+// of any dtype, without total_q (every segment at max_seqlen_q).
+size_t varlen_ws_bytes(int batch, int max_seqlen_q) {
+    if (batch <= 0 || max_seqlen_q <= 0) return 0;
+    const int bm = mxfa::kFwdF32Rows < mxfa::kFwdBf16Rows ? mxfa::kFwdF32Rows : mxfa::kFwdBf16Rows;
+    return mxfa::worklist_bytes(batch, (long long)batch * ((max_seqlen_q + bm - 1) / bm));
+}
+
 mxfa_status launch_fwd(const mxfa::FwdParams& args, int head_dim, mxfa_dtype dtype, hipStream_t stream) {
     mxfa::FwdParams p = args;
     int cus = 0;
@@ -123,7 +139,7 @@ size_t decode_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, i
     const int group = heads_q / heads_kv;
     const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kDecodeRows - 1) / mxfa::kDecodeRows;
     const long long parts = (long long)batch * heads_kv * m_groups * splits;
-    return (size_t)parts * (size_t)mxfa::kDecodeRows * ((size_t)head_dim_v + 2) * sizeof(float);
+    return (size_t)parts * (size_t)mxfa::kDecodeRows * ((size_t)head_dim_v + 3) * sizeof(float);
 }
 
 // Split plan for the standard-head decode: about one work group per compute
@@ -157,7 +173,7 @@ size_t gqa_ws_bytes(int batch, int max_seqlen_q, int heads_q, int heads_kv, int 
     const int group = heads_q / heads_kv;
     const long long m_groups = ((long long)max_seqlen_q * group + mxfa::kGqaRows - 1) / mxfa::kGqaRows;
     const long long parts = (long long)batch * heads_kv * m_groups * splits;
-    return (size_t)parts * (size_t)mxfa::kGqaRows * ((size_t)head_dim + 2) * sizeof(float);
+    return (size_t)parts * (size_t)mxfa::kGqaRows * ((size_t)head_dim + 3) * sizeof(float);
 }
 
 // Checks and launch shared by the contiguous (cu_k) and paged (pg) decode
@@ -296,7 +312,7 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
                             int max_seqlen_k, int total_q, int total_k, int heads_q, int heads_kv, int head_dim,
                             mxfa_dtype dtype, int causal, int window_left, int window_right, float softcap,
-                            float scale, mxfa_stream_t stream) {
+                            float scale, void* workspace, size_t workspace_bytes, mxfa_stream_t stream) {
     g_err[0] = 0;
     if (dtype != MXFA_F32 && dtype != MXFA_BF16) return fail(MXFA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
     if (head_dim != 64 && head_dim != 128) return fail(MXFA_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
@@ -317,6 +333,16 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
     }
     if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
 
+    // The work list of the live q tiles goes into the workspace.
+    const int bm = dtype == MXFA_BF16 ? mxfa::kFwdBf16Rows : mxfa::kFwdF32Rows;
+    const int bn = dtype == MXFA_BF16 ? mxfa::kFwdBf16Keys : mxfa::kFwdF32Keys;
+    const long long list_max = varlen_list_max(batch, max_seqlen_q, total_q, bm);
+    const size_t need = mxfa::worklist_bytes(batch, list_max);
+    if (!workspace || workspace_bytes < need)
+        return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+
     mxfa::FwdParams p = {};
     p.q = q;
     p.k = k;
@@ -325,6 +351,8 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
     p.lse = lse;
     p.cu_q = cu_seqlens_q;
     p.cu_k = cu_seqlens_k;
+    p.worklist = static_cast<const int*>(workspace);
+    p.list_max = list_max;
     p.batch = batch;
     p.seqlen_q = max_seqlen_q;
     p.seqlen_k = max_seqlen_k;
@@ -338,7 +366,27 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
     p.softcap = softcap;
     p.scale = scale;
     fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    mxfa::WorkListParams wp = {};
+    wp.cu_q = cu_seqlens_q;
+    wp.cu_k = cu_seqlens_k;
+    wp.ws = static_cast<int*>(workspace);
+    wp.list_max = list_max;
+    wp.batch = batch;
+    wp.max_seqlen_k = max_seqlen_k;
+    wp.bm = bm;
+    wp.bn = bn;
+    wp.causal = p.causal;
+    wp.window_left = window_left;
+    wp.window_right = window_right;
+    hipError_t e = mxfa::launch_varlen_worklist(wp, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "work-list kernel launch");
     return launch_fwd(p, head_dim, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t mxfa_fwd_varlen_workspace_bytes(int batch, int max_seqlen_q, int heads_q, int head_dim) {
+    (void)heads_q;  // the list holds (segment, q tile) pairs; every query head reads the same list
+    (void)head_dim;
+    return varlen_ws_bytes(batch, max_seqlen_q);
 }
 
 int mxfa_decode_splitkv_num_splits(int batch, int max_seqlen_q, int max_seqlen_k, int heads_q, int heads_kv,

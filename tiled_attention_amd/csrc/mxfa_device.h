@@ -35,6 +35,13 @@ MXFA_DEV uint32_t pack_bf16x2(float lo, float hi) {
 
 MXFA_DEV float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// acc + lo + hi of a packed bf16 pair, in one instruction (v_dot2c_f32_bf16
+// against (1, 1): the products are exact, the sum is an fp32 add).
+MXFA_DEV float add_bf16x2(uint32_t pair, float acc) {
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair), ones, acc, false);
+}
+
 // ---------------------------------------------------------------- math
 
 // 2^x on the hardware transcendental unit (v_exp_f32); exp2(-inf) = 0.
@@ -322,6 +329,39 @@ MXFA_DEV WorkItem map_workgroup(int id, int batch, int heads_kv, int group, int 
 inline long long workgroup_count(int batch, int heads_kv, int group, int n_qtiles) {
     const long long groups = (long long)batch * heads_kv;
     return (long long)kXcds * ((groups + kXcds - 1) / kXcds) * group * n_qtiles;
+}
+
+// Workgroup -> (segment, query head, q tile) of a packed problem from its
+// work list (count, prefix sums, then (segment, q tile) pairs ordered by the
+// key tiles they stream, most first). Units (list entry e, kv head g), in
+// list order, are dealt to the XCDs round-robin; each unit's query heads run
+// as consecutive work groups of one XCD, where they share that K/V in its L2.
+// pair_span as for map_workgroup. Work groups past the list's end get b = -1.
+MXFA_DEV WorkItem map_listed(int id, const int* ws, int batch, int heads_kv, int group, long long list_max,
+                             int pair_span = 0) {
+    const int x = id % kXcds;
+    int n = id / kXcds;
+    const long long per_xcd = (list_max * heads_kv + kXcds - 1) / kXcds * group;
+    if (pair_span > 0 && per_xcd >= 2 * pair_span && n >= pair_span && n < 2 * pair_span)
+        n = 3 * pair_span - 1 - n;
+    const long long u = (long long)(n / group) * kXcds + x;
+    const long long e = u / heads_kv;
+    WorkItem w;
+    w.b = -1;
+    w.h = 0;
+    w.qtile = 0;
+    const int count = ws[0];
+    if (e >= count) return w;
+    const int2 it = reinterpret_cast<const int2*>(ws + 4 + ((batch + 2) & ~1))[e];
+    w.b = it.x;
+    w.qtile = it.y;
+    w.h = (int)(u % heads_kv) * group + n % group;
+    return w;
+}
+
+// Grid size for map_listed.
+inline long long listed_workgroup_count(int heads_kv, int group, long long list_max) {
+    return (long long)kXcds * ((list_max * heads_kv + kXcds - 1) / kXcds) * group;
 }
 
 }  // namespace mxfa

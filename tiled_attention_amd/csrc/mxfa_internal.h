@@ -35,6 +35,27 @@ struct FwdParams {
     float cap_out;           // cap: cap*log2e
     int n_qtiles;            // ceil(seqlen_q / BM), set by the launcher
     int xcd_cus;             // compute units per XCD (pairing of the first dispatch round), 0 = unknown
+    // Packed problems: the work list the list kernel wrote (null for dense)
+    // and an upper bound on its length (sizes the grid).
+    const int* worklist;
+    long long list_max;
+};
+
+// The work-list kernel of a packed forward: (segment, q tile) pairs of bm
+// rows, ordered by the number of bn-key tiles they stream, most first.
+struct WorkListParams {
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int* ws;                 // count, prefix sums, pairs (worklist_bytes())
+    long long list_max;      // pairs the workspace holds; items past it are dropped
+    int batch;
+    int max_seqlen_k;
+    int bm;
+    int bn;
+    int causal;
+    int window_left;
+    int window_right;
+    int shift;               // set by the launcher
 };
 
 // One latent-KV split decode.
@@ -46,7 +67,7 @@ struct DecodeParams {
     const int32_t* cu_q;
     const int32_t* cu_k;
     float* part_acc;         // [batch, m_groups, splits, 64, d_v] fp32
-    float* part_ml;          // [batch, m_groups, splits, 2, 64] fp32 (max, sum)
+    float* part_ml;          // [batch, m_groups, splits, 3, 64] fp32 (max, sum of p, sum of bf16(p))
     int batch;
     int max_seqlen_q;
     int max_seqlen_k;
@@ -85,7 +106,7 @@ struct GqaDecodeParams {
     const int32_t* cu_q;
     const int32_t* cu_k;
     float* part_acc;         // [batch, heads_kv, m_groups, splits, 32, head_dim] fp32 (splits > 1)
-    float* part_ml;          // [batch, heads_kv, m_groups, splits, 2, 32] fp32 (max, sum)
+    float* part_ml;          // [batch, heads_kv, m_groups, splits, 3, 32] fp32 (max, sum of p, sum of bf16(p))
     int batch;
     int total_q;
     int heads_q;
@@ -112,12 +133,20 @@ struct PagedKV {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_varlen_worklist(const WorkListParams& p, hipStream_t stream);
+size_t worklist_bytes(int batch, long long max_items);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_gqa(const GqaDecodeParams& p, int head_dim, hipStream_t stream);
 
 // Accelerator dies (XCDs) of the device, each with its own L2.
 constexpr int kXcdCount = 8;
+
+// Forward tiles: query rows per work group and keys per tile, bf16 and fp32.
+constexpr int kFwdBf16Rows = 128;
+constexpr int kFwdBf16Keys = 64;
+constexpr int kFwdF32Rows = 32;
+constexpr int kFwdF32Keys = 32;
 
 // Rows of one decode work group: (query token, head-in-group) pairs.
 constexpr int kDecodeRows = 64;
