@@ -354,9 +354,20 @@ class ClockSampler:
             self.handle, self.reason = None, f"amdsmi unavailable: {type(e).__name__}: {e}"
 
     def _read(self):
+        """(reported GFX clock, median of the per-XCD current GFX clocks, firmware average GFX clock), MHz."""
         import amdsmi
 
-        return float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+        clk = float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX)["clk"])
+        cur = avg = None
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
+            cur = float(np.median(xs)) if xs else None
+            a = m.get("average_gfxclk_frequency")
+            avg = float(a) if isinstance(a, (int, float)) and 0 < a < 10000 else None
+        except Exception:  # noqa: BLE001 - the metrics table is optional
+            pass
+        return clk, cur, avg
 
     def start(self):
         import threading
@@ -386,9 +397,19 @@ class ClockSampler:
     def summary(self):
         if self.handle is None or not self.samples:
             return {"mhz": None, "note": self.reason or "no samples"}
-        xs = sorted(self.samples)
-        return {"mhz": round(float(np.median(xs)), 1), "min": xs[0], "max": xs[-1], "samples": len(xs),
-                "source": "amdsmi GFX clock, sampled by a host thread during the timed regions"}
+
+        def stats(col):
+            xs = sorted(x[col] for x in self.samples if x[col] is not None)
+            return (round(float(np.median(xs)), 1), xs[0], xs[-1]) if xs else (None, None, None)
+
+        clk, cur, avg = stats(0), stats(1), stats(2)
+        # The per-XCD current clocks are the closest to what the kernels ran at;
+        # the reported clock is the driver's current level.
+        best = cur[0] if cur[0] is not None else clk[0]
+        return {"mhz": best, "samples": len(self.samples),
+                "reported_clk_median_min_max": clk, "xcd_current_gfxclk_median_min_max": cur,
+                "firmware_average_gfxclk_median_min_max": avg,
+                "source": "amdsmi, sampled by a host thread during the timed regions"}
 
 
 def clock_fields(res, peak):
