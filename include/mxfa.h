@@ -123,6 +123,32 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
  */
 size_t mxfa_fwd_varlen_workspace_bytes(int batch, int max_seqlen_q, int heads_q, int head_dim);
 
+/* Bytes of the static device array mxfa_fwd_varlen_noalloc keeps its work list in. */
+#define MXFA_NOALLOC_SCRATCH_BYTES (1u << 20)
+
+/*
+ * Allocation-free packed forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. Same arguments, computation and result as
+ * mxfa_fwd_varlen (bit for bit), minus the workspace: the work list goes into
+ * a static device array of the library, MXFA_NOALLOC_SCRATCH_BYTES bytes, one
+ * copy per GPU, held from the library's load until the process ends (its
+ * address is looked up once per device, on the first call made with that
+ * device current). The list holds one entry per query tile, about 130,000
+ * of them (16.7 million query tokens at the bf16 kernel's 128-row tiles,
+ * 4.2 million at the fp32 kernel's 32); a problem whose list would not fit
+ * returns MXFA_ERR_WORKSPACE with nothing enqueued. The call allocates nothing and calls no allocating
+ * routine. Every call on a GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs clearing): calls that overlap on one
+ * GPU -- on streams that do not order them -- race and must not be made.
+ */
+mxfa_status mxfa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    int batch, int max_seqlen_q, int max_seqlen_k, int total_q,
+                                    int total_k, int heads_q, int heads_kv, int head_dim,
+                                    mxfa_dtype dtype, int causal, int window_left, int window_right,
+                                    float softcap, float scale, mxfa_stream_t stream);
+
 /*
  * Split-KV decode over a shared latent KV (the kernelbot amd-mixed-mla
  * submission 588924 page: _flash_splitk then _reduce_splitk; the split /

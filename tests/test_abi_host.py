@@ -250,3 +250,17 @@ def test_workspace_bytes_is_arithmetic(lib, batch, mq, mk, hq, hkv, splits):
     want = batch * hkv * groups * splits * 64 * (512 + 3) * 4
     assert mx.mxfa_decode_splitkv_workspace_bytes(batch, mq, mk, hq, hkv, 512, splits) == want
     assert mx.mxfa_decode_splitkv_num_splits(batch, mq, mk, hq, hkv, splits) == splits
+
+
+def test_noalloc_varlen_rejects_lists_beyond_its_static_array(lib):
+    # 64 segments of up to 2^21 tokens: about 2^20 query tiles, far beyond the
+    # static array's 2^20 bytes. Refused on the host, before any HIP call.
+    st = lib.mxfa_fwd_varlen_noalloc(A, A, A, A, A, A, A, 64, 1 << 21, 1 << 21, 1 << 27, 1 << 27, 4, 2, 128, 1, 1,
+                                     -1, -1, 0.0, 0.1, None)
+    assert st == WORKSPACE
+    assert "allocation-free" in lib.mxfa_last_error().decode()
+    # Empty calls do nothing and succeed; bad arguments are refused as by mxfa_fwd_varlen.
+    assert lib.mxfa_fwd_varlen_noalloc(A, A, A, A, A, A, A, 0, 0, 0, 0, 0, 4, 2, 128, 1, 1, -1, -1, 0.0, 0.1,
+                                       None) == OK
+    assert lib.mxfa_fwd_varlen_noalloc(A, A, A, A, A, A, A, 2, 16, 16, 20, 20, 4, 2, 80, 1, 1, -1, -1, 0.0, 0.1,
+                                       None) == UNSUPPORTED

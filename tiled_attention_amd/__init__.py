@@ -22,6 +22,7 @@ __all__ = [
     "mxfa_fwd",
     "mxfa_fwd_varlen",
     "mxfa_fwd_varlen_workspace_bytes",
+    "mxfa_fwd_varlen_noalloc",
     "mxfa_decode_splitkv",
     "mxfa_decode_splitkv_paged",
     "mxfa_decode_splitkv_fp8",
@@ -48,6 +49,7 @@ _SIGNATURES = {
     "mxfa_fwd": (_c_int, [_vp] * 5 + [_c_int] * 10 + [_c_float, _c_float, _vp]),
     "mxfa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp, _sz, _vp]),
     "mxfa_fwd_varlen_workspace_bytes": (_sz, [_c_int] * 4),
+    "mxfa_fwd_varlen_noalloc": (_c_int, [_vp] * 7 + [_c_int] * 12 + [_c_float, _c_float, _vp]),
     "mxfa_decode_splitkv": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_paged": (_c_int, [_vp] * 7 + [_c_int] * 14 + [_c_float, _c_float, _c_int, _vp, _sz, _vp]),
     "mxfa_decode_splitkv_fp8": (_c_int, [_vp] * 6 + [_c_int] * 12 + [_c_float] * 3 + [_c_int, _vp, _sz, _vp]),
@@ -202,6 +204,37 @@ def mxfa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                  hkv, d, _dtype_code(q), int(bool(causal)), int(window[0]), int(window[1]),
                                  float(softcap), _scale(scale, d), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return out, lse
+
+
+def mxfa_fwd_varlen_noalloc(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *, causal=False,
+                            window=(-1, -1), softcap=0.0, scale=None, out=None, lse=None, return_lse=True):
+    """mxfa_fwd_varlen without a workspace: the library keeps the work list in its own static device
+    array (for callers that cannot allocate). Pass ``out`` (and ``lse``) to keep the call free of
+    allocations; otherwise they are allocated here. Same result as mxfa_fwd_varlen, bit for bit.
+    """
+    lib = load_library()
+    _need(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, "q, k, v must be [T, H, d]")
+    tq, hq, d = q.shape
+    tk, hkv = k.shape[0], k.shape[1]
+    _need(k.shape == (tk, hkv, d) and v.shape == (tk, hkv, d), "k/v shapes do not match q")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v must share a dtype")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32, "cu_seqlens must be int32")
+    _need(cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape, "cu_seqlens shapes differ")
+    batch = cu_seqlens_q.shape[0] - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(lse is None or (lse.shape == (hq, tq) and lse.dtype == torch.float32), "lse must be [Hq,Tq] fp32")
+    dev = _tensors_ok(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k)
+    with torch.cuda.device(dev):
+        st = lib.mxfa_fwd_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                         _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), tq, tk,
+                                         hq, hkv, d, _dtype_code(q), int(bool(causal)), int(window[0]),
+                                         int(window[1]), float(softcap), _scale(scale, d), _stream(dev))
     _check(st)
     return out, lse
 

@@ -256,6 +256,125 @@ mxfa_status decode_common(const void* q, const void* kv, void* o, float* lse, co
     return MXFA_OK;
 }
 
+// Static scratch of the allocation-free entry point: one copy per GPU, in
+// device memory from the library's load until the process ends. Host code
+// uses only the address hipGetSymbolAddress gives for the current device.
+__device__ __attribute__((aligned(256))) char scratch[MXFA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of this GPU's copy of scratch, looked up once per device
+// with that device current. Null (and *err set) if the lookup fails.
+void* scratch_device_ptr(hipError_t* err) {
+    static std::mutex mu;
+    static void* ptrs[64] = {nullptr};
+    int dev = 0;
+    *err = hipGetDevice(&dev);
+    if (*err != hipSuccess) return nullptr;
+    if (dev < 0 || dev >= 64) {
+        *err = hipErrorInvalidDevice;
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* ptr = nullptr;
+        *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (*err != hipSuccess || !ptr) {
+            if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+            return nullptr;
+        }
+        ptrs[dev] = ptr;
+    }
+    return ptrs[dev];
+}
+
+// Checks and launches of the packed forward. static_scratch: the work list
+// goes into this library's static device array (the allocation-free entry
+// point) instead of the caller's workspace.
+mxfa_status varlen_common(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch, int max_seqlen_q,
+                          int max_seqlen_k, int total_q, int total_k, int heads_q, int heads_kv, int head_dim,
+                          mxfa_dtype dtype, int causal, int window_left, int window_right, float softcap,
+                          float scale, void* workspace, size_t workspace_bytes, bool static_scratch,
+                          mxfa_stream_t stream) {
+    if (dtype != MXFA_F32 && dtype != MXFA_BF16) return fail(MXFA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (head_dim != 64 && head_dim != 128) return fail(MXFA_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
+    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+        return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
+    if (max_seqlen_q > total_q || max_seqlen_k > total_k)
+        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
+    mxfa_status st = check_common(heads_q, heads_kv, window_left, window_right, softcap, scale);
+    if (st != MXFA_OK) return st;
+    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return MXFA_OK;
+    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) != MXFA_OK) return st;
+    if ((st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)) != MXFA_OK) return st;
+    if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
+    if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
+    if (total_k > 0) {
+        if ((st = check_tensor(k, "k", 16)) != MXFA_OK) return st;
+        if ((st = check_tensor(v, "v", 16)) != MXFA_OK) return st;
+    }
+    if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+
+    // The work list of the live q tiles goes into the workspace.
+    const int bm = dtype == MXFA_BF16 ? mxfa::kFwdBf16Rows : mxfa::kFwdF32Rows;
+    const int bn = dtype == MXFA_BF16 ? mxfa::kFwdBf16Keys : mxfa::kFwdF32Keys;
+    const long long list_max = varlen_list_max(batch, max_seqlen_q, total_q, bm);
+    const size_t need = mxfa::worklist_bytes(batch, list_max);
+    if (static_scratch) {
+        if (need > (size_t)MXFA_NOALLOC_SCRATCH_BYTES)
+            return fail(MXFA_ERR_WORKSPACE,
+                        "the work list needs %zu bytes; the allocation-free call holds at most %u "
+                        "(use mxfa_fwd_varlen with a workspace)",
+                        need, (unsigned)MXFA_NOALLOC_SCRATCH_BYTES);
+        hipError_t e = hipSuccess;
+        workspace = scratch_device_ptr(&e);
+        if (!workspace) return hip_fail(e, "address of the static scratch array");
+        workspace_bytes = MXFA_NOALLOC_SCRATCH_BYTES;
+    }
+    if (!workspace || workspace_bytes < need)
+        return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                    workspace ? workspace_bytes : 0);
+    if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+
+    mxfa::FwdParams p = {};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = o;
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.worklist = static_cast<const int*>(workspace);
+    p.list_max = list_max;
+    p.batch = batch;
+    p.seqlen_q = max_seqlen_q;
+    p.seqlen_k = max_seqlen_k;
+    p.total_q = total_q;
+    p.heads_q = heads_q;
+    p.heads_kv = heads_kv;
+    p.group = heads_q / heads_kv;
+    p.causal = causal ? 1 : 0;
+    p.window_left = window_left;
+    p.window_right = window_right;
+    p.softcap = softcap;
+    p.scale = scale;
+    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
+    mxfa::WorkListParams wp = {};
+    wp.cu_q = cu_seqlens_q;
+    wp.cu_k = cu_seqlens_k;
+    wp.ws = static_cast<int*>(workspace);
+    wp.list_max = list_max;
+    wp.batch = batch;
+    wp.max_seqlen_k = max_seqlen_k;
+    wp.bm = bm;
+    wp.bn = bn;
+    wp.causal = p.causal;
+    wp.window_left = window_left;
+    wp.window_right = window_right;
+    hipError_t e = mxfa::launch_varlen_worklist(wp, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "work-list kernel launch");
+    return launch_fwd(p, head_dim, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -314,73 +433,20 @@ mxfa_status mxfa_fwd_varlen(const void* q, const void* k, const void* v, void* o
                             mxfa_dtype dtype, int causal, int window_left, int window_right, float softcap,
                             float scale, void* workspace, size_t workspace_bytes, mxfa_stream_t stream) {
     g_err[0] = 0;
-    if (dtype != MXFA_F32 && dtype != MXFA_BF16) return fail(MXFA_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
-    if (head_dim != 64 && head_dim != 128) return fail(MXFA_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", head_dim);
-    if (batch < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
-        return fail(MXFA_ERR_INVALID_ARG, "batch, max lengths and totals must be >= 0");
-    if (max_seqlen_q > total_q || max_seqlen_k > total_k)
-        return fail(MXFA_ERR_INVALID_ARG, "max_seqlen exceeds the total token count");
-    mxfa_status st = check_common(heads_q, heads_kv, window_left, window_right, softcap, scale);
-    if (st != MXFA_OK) return st;
-    if (batch == 0 || total_q == 0 || max_seqlen_q == 0) return MXFA_OK;
-    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) != MXFA_OK) return st;
-    if ((st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)) != MXFA_OK) return st;
-    if ((st = check_tensor(q, "q", 16)) != MXFA_OK) return st;
-    if ((st = check_tensor(o, "o", 16)) != MXFA_OK) return st;
-    if (total_k > 0) {
-        if ((st = check_tensor(k, "k", 16)) != MXFA_OK) return st;
-        if ((st = check_tensor(v, "v", 16)) != MXFA_OK) return st;
-    }
-    if (lse && !aligned(lse, 4)) return fail(MXFA_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    return varlen_common(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
+                         total_k, heads_q, heads_kv, head_dim, dtype, causal, window_left, window_right, softcap,
+                         scale, workspace, workspace_bytes, false, stream);
+}
 
-    // The work list of the live q tiles goes into the workspace.
-    const int bm = dtype == MXFA_BF16 ? mxfa::kFwdBf16Rows : mxfa::kFwdF32Rows;
-    const int bn = dtype == MXFA_BF16 ? mxfa::kFwdBf16Keys : mxfa::kFwdF32Keys;
-    const long long list_max = varlen_list_max(batch, max_seqlen_q, total_q, bm);
-    const size_t need = mxfa::worklist_bytes(batch, list_max);
-    if (!workspace || workspace_bytes < need)
-        return fail(MXFA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                    workspace ? workspace_bytes : 0);
-    if (!aligned(workspace, 16)) return fail(MXFA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-
-    mxfa::FwdParams p = {};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.o = o;
-    p.lse = lse;
-    p.cu_q = cu_seqlens_q;
-    p.cu_k = cu_seqlens_k;
-    p.worklist = static_cast<const int*>(workspace);
-    p.list_max = list_max;
-    p.batch = batch;
-    p.seqlen_q = max_seqlen_q;
-    p.seqlen_k = max_seqlen_k;
-    p.total_q = total_q;
-    p.heads_q = heads_q;
-    p.heads_kv = heads_kv;
-    p.group = heads_q / heads_kv;
-    p.causal = causal ? 1 : 0;
-    p.window_left = window_left;
-    p.window_right = window_right;
-    p.softcap = softcap;
-    p.scale = scale;
-    fill_scaling(scale, softcap, &p.x_mul, &p.cap_mul, &p.cap_out);
-    mxfa::WorkListParams wp = {};
-    wp.cu_q = cu_seqlens_q;
-    wp.cu_k = cu_seqlens_k;
-    wp.ws = static_cast<int*>(workspace);
-    wp.list_max = list_max;
-    wp.batch = batch;
-    wp.max_seqlen_k = max_seqlen_k;
-    wp.bm = bm;
-    wp.bn = bn;
-    wp.causal = p.causal;
-    wp.window_left = window_left;
-    wp.window_right = window_right;
-    hipError_t e = mxfa::launch_varlen_worklist(wp, reinterpret_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "work-list kernel launch");
-    return launch_fwd(p, head_dim, dtype, reinterpret_cast<hipStream_t>(stream));
+mxfa_status mxfa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int batch,
+                                    int max_seqlen_q, int max_seqlen_k, int total_q, int total_k, int heads_q,
+                                    int heads_kv, int head_dim, mxfa_dtype dtype, int causal, int window_left,
+                                    int window_right, float softcap, float scale, mxfa_stream_t stream) {
+    g_err[0] = 0;
+    return varlen_common(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k, total_q,
+                         total_k, heads_q, heads_kv, head_dim, dtype, causal, window_left, window_right, softcap,
+                         scale, nullptr, 0, true, stream);
 }
 
 size_t mxfa_fwd_varlen_workspace_bytes(int batch, int max_seqlen_q, int heads_q, int head_dim) {
