@@ -6,8 +6,11 @@ the dense causal prefill (B=4, H=16, S=2048, d=128, bf16) through mxfa_fwd,
 and the latent-KV split decode (batch 128, q_len 4, 16 heads, 576/512,
 kv_len 8192, bf16) through mxfa_decode_splitkv. Inputs are generated with the
 seeded recipe of the ``workloads`` module and are resident in HBM before the
-timed region. Each call is timed with HIP events on the stream it is launched
-on, over ``--steps`` launches after ``--warmup`` untimed ones.
+timed region. Each workload first runs back to back for about ``--settle-ms``
+of GPU time (the chip's clock then settles at its sustained level for that
+load, which the bench samples and reports), then ``--warmup`` untimed calls,
+then ``--repeats`` timed regions of exactly ``--steps`` calls, each bracketed
+by HIP events on the stream the calls are launched on.
 
 Prints ONE JSON line. ``value`` is the prefill's algorithmic TFLOP/s (4*d
 flops per visible (query, key) pair); the ``decode`` object carries the
@@ -16,7 +19,7 @@ decode's algorithmic HBM GB/s (Q + latent KV + O + LSE bytes, each once).
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of the same
 prefill workload on the host cores.
 
-Options: --gpus N (only 1 is supported), --steps K, --warmup W,
+Options: --gpus N (only 1 is supported), --steps K, --warmup W, --settle-ms T,
 --workloads a,b,... (default: causal_prefill_bf16,mla_decode_bf16; "all"
 adds the other configurations as extra lines in ``extra``),
 --no-cpu-baseline, --cpu-seconds S.
@@ -285,13 +288,66 @@ class Runner:
             del inp
         torch.cuda.synchronize()
 
-    def time(self, steps, warmup, repeats=1, sampler=None):
+    def settle(self, ms_target, probes=8):
+        """Back-to-back calls for about ``ms_target`` ms of GPU time; returns (calls, ms, clock).
+
+        The chip's shader clock follows its load: after an idle gap the first
+        calls of a burst run at a clock the chip does not hold. The bench runs
+        this before the warmup calls so that the timed calls see the sustained
+        clock. The run is cut into ``probes`` chunks. While each chunk runs,
+        the library's shader-clock probe (one wave counting shader cycles
+        against the 100 MHz real-time counter for 1 ms) runs alongside it on a
+        second stream and reads the clock under this load; ``clock``
+        summarises those readings (MHz). A probe run between calls instead
+        reads the idle clock (~2.4 GHz), since the clock recovers within
+        microseconds; the side-by-side reading still counts the gaps between
+        calls and so reads a few percent above the kernels' own clock.
+        """
+        import torch
+
+        import tiled_attention_amd as mx
+
+        if ms_target <= 0:
+            return 0, 0.0, {"mhz": None, "note": "no settle run"}
+        stream = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(5):
+            self.call()
+        end.record(stream)
+        torch.cuda.synchronize()
+        per = max(start.elapsed_time(end) / 5, 1e-3)
+        chunk = max(1, int(ms_target / per / probes))
+        buf = torch.zeros(2 * probes, dtype=torch.int64, device="cuda:0")
+        start.record(stream)
+        for i in range(probes):
+            for _ in range(chunk):
+                self.call()
+            # The host is ahead of the GPU here: the probe runs beside the
+            # chunk's remaining calls.
+            with torch.cuda.stream(side):
+                mx.mxfa_clock_probe(buf[2 * i:2 * i + 2], 1000)
+            if i + 1 < probes:
+                torch.cuda.synchronize()  # keep the host within one chunk of the GPU
+        end.record(stream)
+        torch.cuda.synchronize()
+        v = buf.cpu().numpy().reshape(-1, 2).astype(np.float64)
+        mhz = [round(float(c / t * 100.0), 1) for c, t in v if t > 0]
+        clock = {"mhz": round(float(np.median(mhz)), 1) if mhz else None, "probes_mhz": mhz,
+                 "source": "in-kernel probe (s_memtime cycles / s_memrealtime ticks over 1 ms) on a second "
+                           f"stream beside each of {probes} chunks of {chunk} back-to-back calls; reads a few "
+                           "percent above the kernels' own clock (it also counts the gaps between calls)"}
+        return chunk * probes, start.elapsed_time(end), clock
+
+    def time(self, steps, warmup, repeats=1):
         """ms per call of each of ``repeats`` timed regions of exactly ``steps`` calls.
 
         ``warmup`` untimed calls come first. Each region is bracketed by HIP
         events on the stream the calls are launched on, with a device
-        synchronisation on both sides. ``sampler`` (a ClockSampler) reads the
-        shader clock while the regions run.
+        synchronisation on both sides.
         """
         import torch
 
@@ -300,126 +356,27 @@ class Runner:
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         out = []
-        if sampler:
-            sampler.start()
-        try:
-            for _ in range(repeats):
-                start = torch.cuda.Event(enable_timing=True)
-                end = torch.cuda.Event(enable_timing=True)
-                torch.cuda.synchronize()
-                start.record(stream)
-                for _ in range(steps):
-                    self.call()
-                end.record(stream)
-                torch.cuda.synchronize()
-                out.append(start.elapsed_time(end) / steps)  # ms per call
-        finally:
-            if sampler:
-                sampler.stop()
+        for _ in range(repeats):
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(steps):
+                self.call()
+            end.record(stream)
+            torch.cuda.synchronize()
+            out.append(start.elapsed_time(end) / steps)  # ms per call
         return out
 
 
-class ClockSampler:
-    """The GPU's shader (GFX) clock as the driver reports it, read through amdsmi
-    from a host thread while timed regions run.
-
-    The device is matched to cuda:0 by its PCI address. When amdsmi is missing
-    or cannot read the device, ``summary()`` says so instead of giving figures.
-    """
-
-    def __init__(self):
-        self.handle, self.reason = None, None
-        self.samples = []
-        self._stop = None
-        self._thread = None
-        try:
-            import amdsmi
-            import torch
-
-            amdsmi.amdsmi_init()
-            props = torch.cuda.get_device_properties(0)
-            want = (int(getattr(props, "pci_domain_id", 0)), int(props.pci_bus_id), int(props.pci_device_id))
-            for h in amdsmi.amdsmi_get_processor_handles():
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
-                dom, bus, devfn = bdf.split(":")
-                if (int(dom, 16), int(bus, 16), int(devfn.split(".")[0], 16)) == want:
-                    self.handle = h
-                    break
-            if self.handle is None:
-                self.reason = f"no amdsmi device at PCI {want}"
-            else:
-                self._read()  # one read up front, so that an unreadable clock shows here
-            self._amdsmi = amdsmi
-        except Exception as e:  # noqa: BLE001 - any failure only means "no clock figure"
-            self.handle, self.reason = None, f"amdsmi unavailable: {type(e).__name__}: {e}"
-
-    def _read(self):
-        """(reported GFX clock, median of the per-XCD current GFX clocks, firmware average GFX clock), MHz."""
-        import amdsmi
-
-        clk = float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.GFX)["clk"])
-        cur = avg = None
-        try:
-            m = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
-            xs = [float(x) for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
-            cur = float(np.median(xs)) if xs else None
-            a = m.get("average_gfxclk_frequency")
-            avg = float(a) if isinstance(a, (int, float)) and 0 < a < 10000 else None
-        except Exception:  # noqa: BLE001 - the metrics table is optional
-            pass
-        return clk, cur, avg
-
-    def start(self):
-        import threading
-
-        if self.handle is None:
-            return
-        self.samples = []
-        self._stop = threading.Event()
-
-        def loop():
-            while not self._stop.is_set():
-                try:
-                    self.samples.append(self._read())
-                except Exception:  # noqa: BLE001
-                    return
-                self._stop.wait(0.0005)
-
-        self._thread = threading.Thread(target=loop, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-            self._thread = None
-
-    def summary(self):
-        if self.handle is None or not self.samples:
-            return {"mhz": None, "note": self.reason or "no samples"}
-
-        def stats(col):
-            xs = sorted(x[col] for x in self.samples if x[col] is not None)
-            return (round(float(np.median(xs)), 1), xs[0], xs[-1]) if xs else (None, None, None)
-
-        clk, cur, avg = stats(0), stats(1), stats(2)
-        # The per-XCD current clocks are the closest to what the kernels ran at;
-        # the reported clock is the driver's current level.
-        best = cur[0] if cur[0] is not None else clk[0]
-        return {"mhz": best, "samples": len(self.samples),
-                "reported_clk_median_min_max": clk, "xcd_current_gfxclk_median_min_max": cur,
-                "firmware_average_gfxclk_median_min_max": avg,
-                "source": "amdsmi, sampled by a host thread during the timed regions"}
-
-
 def clock_fields(res, peak):
-    """Shader clock seen during the timed regions, and the MFMA peak scaled to it.
+    """Shader clock seen under sustained load of the workload, and the MFMA peak scaled to it.
 
     The dense bf16 MFMA peak assumes 2.4 GHz; at a lower clock the chip's
     attainable peak is lower in proportion.
     """
     mhz = (res.get("clock") or {}).get("mhz")
-    out = {"clock_mhz": mhz, "peak_clock_mhz": 2400.0}
+    out = {"clock_mhz": mhz, "clock_probes_mhz": (res.get("clock") or {}).get("probes_mhz"), "peak_clock_mhz": 2400.0}
     if mhz:
         peak_at = peak * mhz / 2400.0
         out["peak_at_clock"] = round(peak_at, 1)
@@ -516,13 +473,17 @@ def _cpu_model():
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # Long timed regions right after a long warmup: after any idle gap the
+    # chip restarts at a lower shader clock and takes ~10-25 ms of continuous
+    # load to reach its sustained one, which short regions would mostly miss.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--repeats", type=int, default=5,
                     help="timed regions of --steps calls each; the figures are their median")
     ap.add_argument("--workloads", default=f"{PRIMARY},{DECODE}")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-clock", action="store_true", help="do not sample the shader clock")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="GPU time of back-to-back calls before the warmup of each workload (sustained clock)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
@@ -550,19 +511,21 @@ def main():
     if PRIMARY not in names:
         names.insert(0, PRIMARY)
 
-    sampler = None if args.no_clock else ClockSampler()
     results = {}
     for name in names:
         print(f"[bench] {name}: preparing inputs", file=sys.stderr, flush=True)
         r = Runner(name)
-        reps = r.time(args.steps, args.warmup, max(1, args.repeats), sampler)
+        settle_calls, settle_ms, clock = r.settle(args.settle_ms)
+        reps = r.time(args.steps, args.warmup, max(1, args.repeats))
         ms = float(np.median(reps))
         res = {
             "workload": name,
+            "settle_calls": settle_calls,
+            "settle_ms": round(settle_ms, 1),
             "ms": round(ms, 4),
             "ms_mean": round(float(np.mean(reps)), 4),
             "ms_repeats": [round(x, 4) for x in reps],
-            "clock": sampler.summary() if sampler else None,
+            "clock": clock,
             "tflops": r.flops / (ms * 1e-3) / 1e12,
             "gbs": r.bytes / (ms * 1e-3) / 1e9,
             "flops_per_call": r.flops,
@@ -598,6 +561,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": p["ms"],
         "higher_is_better": True,
         "scaling": "weak",

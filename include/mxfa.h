@@ -285,6 +285,20 @@ const char* mxfa_last_error(void);
 /* Library version string, e.g. "mxfa 0.1.0 gfx950". */
 const char* mxfa_version(void);
 
+/*
+ * Measurement aid, not part of attention: the shader clock the chip runs at.
+ * One wave counts shader-clock cycles (s_memtime) against the fixed 100 MHz
+ * real-time counter (s_memrealtime) for interval_us microseconds (1..1000)
+ * and writes two uint64 values to out_device (device memory, 8-byte
+ * aligned, caller-owned): [0] the cycles, [1] the real-time ticks (10 ns
+ * each); cycles / ticks * 100 is the clock in MHz over the interval.
+ * Enqueued on `stream` like the other calls: between a workload's calls it
+ * reads the clock the chip holds under that load. Returns
+ * MXFA_ERR_INVALID_ARG for a null or misaligned pointer or an interval out
+ * of range, MXFA_ERR_HIP if the launch fails.
+ */
+mxfa_status mxfa_clock_probe(void* out_device, int interval_us, mxfa_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

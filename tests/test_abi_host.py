@@ -63,7 +63,7 @@ def test_header_declares_the_entry_points():
               "mxfa_decode_splitkv_gqa", "mxfa_decode_splitkv_gqa_workspace_bytes",
               "mxfa_decode_splitkv_gqa_num_splits",
               "mxfa_decode_splitkv_workspace_bytes",
-              "mxfa_decode_splitkv_num_splits", "mxfa_last_error", "mxfa_version"):
+              "mxfa_decode_splitkv_num_splits", "mxfa_last_error", "mxfa_version", "mxfa_clock_probe"):
         assert n in names, n
 
 
@@ -82,6 +82,12 @@ def test_binding_signatures_match_header():
 
 def test_version(lib):
     assert mx.mxfa_version().startswith("mxfa")
+
+
+@pytest.mark.parametrize("out,us", [(None, 50), (A + 4, 50), (A, 0), (A, 1001), (A, -5)])
+def test_clock_probe_host_checks(lib, out, us):
+    assert lib.mxfa_clock_probe(out, us, None) == INVALID
+    assert lib.mxfa_last_error().decode()
 
 
 def fwd(lib, **kw):

@@ -32,6 +32,7 @@ __all__ = [
     "mxfa_decode_splitkv_workspace_bytes",
     "mxfa_decode_splitkv_num_splits",
     "mxfa_version",
+    "mxfa_clock_probe",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +61,7 @@ _SIGNATURES = {
     "mxfa_decode_splitkv_num_splits": (_c_int, [_c_int] * 6),
     "mxfa_last_error": (ctypes.c_char_p, []),
     "mxfa_version": (ctypes.c_char_p, []),
+    "mxfa_clock_probe": (_c_int, [_vp, _c_int, _vp]),
 }
 
 
@@ -140,6 +142,21 @@ def _scale(scale, head_dim):
 
 def mxfa_version() -> str:
     return load_library().mxfa_version().decode()
+
+
+def mxfa_clock_probe(out, interval_us=50):
+    """Enqueue the shader-clock probe on the current stream of ``out``'s device.
+
+    ``out`` is an int64 GPU tensor with at least 2 elements; [0] receives the
+    shader-clock cycles, [1] the 100 MHz real-time ticks of the interval, so
+    ``out[0] / out[1] * 100`` is the clock in MHz once the stream has run it.
+    """
+    lib = load_library()
+    _need(out.dtype == torch.int64 and out.numel() >= 2, "out must be an int64 tensor of >= 2 elements")
+    dev = _tensors_ok(out)
+    with torch.cuda.device(dev):
+        st = lib.mxfa_clock_probe(_ptr(out), int(interval_us), _stream(dev))
+    _check(st)
 
 
 def mxfa_fwd(q, k, v, *, causal=False, window=(-1, -1), softcap=0.0, scale=None, out=None, lse=None,

@@ -383,6 +383,17 @@ const char* mxfa_last_error(void) { return g_err; }
 
 const char* mxfa_version(void) { return "mxfa 0.1.0 gfx950"; }
 
+mxfa_status mxfa_clock_probe(void* out_device, int interval_us, mxfa_stream_t stream) {
+    g_err[0] = 0;
+    if (interval_us < 1 || interval_us > 1000) return fail(MXFA_ERR_INVALID_ARG, "interval_us must be in [1, 1000]");
+    mxfa_status st = check_tensor(out_device, "out_device", 8);
+    if (st != MXFA_OK) return st;
+    hipError_t e = mxfa::launch_clock_probe(static_cast<unsigned long long*>(out_device), (unsigned)interval_us * 100u,
+                                            reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "clock probe launch");
+    return MXFA_OK;
+}
+
 mxfa_status mxfa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int seqlen_q,
                      int seqlen_k, int heads_q, int heads_kv, int head_dim, mxfa_dtype dtype, int causal,
                      int window_left, int window_right, float softcap, float scale, mxfa_stream_t stream) {

@@ -133,6 +133,10 @@ struct PagedKV {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams& p, int head_dim, hipStream_t stream);
+// Shader-clock probe (clock_probe.hip): out[0] = shader-clock cycles,
+// out[1] = 100 MHz real-time ticks over an interval of `ticks` ticks.
+hipError_t launch_clock_probe(unsigned long long* out, unsigned ticks, hipStream_t stream);
+
 hipError_t launch_varlen_worklist(const WorkListParams& p, hipStream_t stream);
 size_t worklist_bytes(int batch, long long max_items);
 hipError_t launch_fwd_f32(const FwdParams& p, int head_dim, hipStream_t stream);
