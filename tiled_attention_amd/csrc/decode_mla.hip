@@ -262,11 +262,12 @@ void decode_split_kernel(const DecodeParams p) {
             uint32_t h[8];
 #pragma unroll
             for (int wd = 0; wd < 4; ++wd) {
-                const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[n][wd], false);
-                const f32x2_t c = __builtin_amdgcn_cvt_pk_f32_fp8((int)r.v[n][wd], true);
-                // bf16 = the high half of the float (exact here).
-                h[2 * wd] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-                h[2 * wd + 1] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+                // Two e4m3 codes (bytes 0-1, then 2-3) to two bf16 each, scale 1:
+                // every e4m3 value is exact in bf16.
+                h[2 * wd] = __builtin_bit_cast(uint32_t,
+                                               __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[n][wd], 1.0f, false));
+                h[2 * wd + 1] = __builtin_bit_cast(uint32_t,
+                                                   __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[n][wd], 1.0f, true));
             }
             typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
             *(lds_u32x4*)to_lds(stage + lo8[n]) = u32x4_t{h[0], h[1], h[2], h[3]};
