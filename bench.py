@@ -197,6 +197,49 @@ def pmc_summarize(fetch_csv, write_csv, copy_mb):
     print(json.dumps(out, indent=1))
 
 
+def trace_summarize(trace_csv, names, tail=1000, probes=8):
+    """Per-dispatch durations of a rocprofv3 kernel trace of a bench run, by workload and kernel.
+
+    The trace is cut into the bench's workloads (named in its order by
+    ``names``): a workload ends once its ``probes`` clock probes have run and
+    a kernel it did not launch appears. Prints one markdown row per
+    (workload, kernel, grid): calls, mean over all dispatches, and median /
+    min / max over the last ``tail`` dispatches (a workload's timed calls
+    come last).
+    """
+    import csv
+
+    rows = []
+    with open(trace_csv) as f:
+        for row in csv.DictReader(f):
+            rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]), row["Kernel_Name"],
+                         int(row["Grid_Size_X"]) // max(1, int(row["Workgroup_Size_X"]))))
+    rows.sort()
+    segments = [{"groups": {}, "probes": 0}]
+    for st, en, name, wgs in rows:
+        short = name.replace("(anonymous namespace)::", "").replace("mxfa::", "")
+        short = (short[5:] if short.startswith("void ") else short).split("(")[0]
+        if short.startswith("at::") or "copyBuffer" in short:
+            continue  # torch's fills and copies of the harness
+        seg = segments[-1]
+        if short == "clock_probe_kernel":
+            seg["probes"] += 1
+            continue
+        key = (short, wgs)
+        if seg["probes"] >= probes and key not in seg["groups"]:
+            seg = {"groups": {}, "probes": 0}
+            segments.append(seg)
+        seg["groups"].setdefault(key, []).append((en - st) / 1000.0)
+    print("| Workload | Kernel | Work groups | Calls | Mean, all (us) | Median, last %d (us) | Min | Max |" % tail)
+    print("|---|---|---|---|---|---|---|---|")
+    for i, seg in enumerate(segments):
+        label = names[i] if i < len(names) else f"segment {i}"
+        for (short, wgs), v in seg["groups"].items():
+            allv, last = np.array(v), np.array(v[-tail:])
+            print(f"| {label} | `{short}` | {wgs} | {len(v)} | {allv.mean():.1f} | {np.median(last):.1f} | "
+                  f"{last.min():.1f} | {last.max():.1f} |")
+
+
 def load_traffic(kernel):
     """HBM traffic per launch from committed rocprofv3 PMC runs, if taken on this exact source."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -470,6 +513,17 @@ def _cpu_model():
     return "unknown"
 
 
+def workload_names(spec):
+    """The workloads a --workloads value runs, in the bench's order."""
+    names = spec.split(",")
+    if names == ["all"]:
+        names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16",
+                 "chunked_prefill_bf16", "paged_mla_decode_bf16", "gqa_decode_bf16", "mla_decode_fp8"]
+    if PRIMARY not in names:
+        names.insert(0, PRIMARY)
+    return names
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,7 +541,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mb", type=int, default=0)
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--trace-summarize", metavar="KERNEL_TRACE_CSV",
+                    help="print per-(kernel, grid) durations of a rocprofv3 --kernel-trace csv and exit")
     args = ap.parse_args()
+    if args.trace_summarize:
+        trace_summarize(args.trace_summarize, workload_names(args.workloads))
+        return
     if args.pmc_summarize:
         if args.copy_probe_mb <= 0:
             raise SystemExit("--pmc-summarize needs --copy-probe-mb (the size of the calibration copy)")
@@ -504,12 +563,7 @@ def main():
     import tiled_attention_amd as mx
 
     mx.load_library()  # fails loudly when the HIP library is not built
-    names = args.workloads.split(",")
-    if names == ["all"]:
-        names = [PRIMARY, DECODE, "single_head_f32", "varlen_gqa_causal_bf16", "window_softcap_bf16",
-                 "chunked_prefill_bf16", "paged_mla_decode_bf16", "gqa_decode_bf16", "mla_decode_fp8"]
-    if PRIMARY not in names:
-        names.insert(0, PRIMARY)
+    names = workload_names(args.workloads)
 
     results = {}
     for name in names:

@@ -128,3 +128,43 @@ def test_committed_traffic_figures_are_tagged_with_a_known_family():
     assert fams and set(fams) <= set(bench.PMC_KERNELS)
     for k in fams:
         assert abs(rec[k]["bytes_per_launch"] - rec[k]["fetch_bytes"] - rec[k]["write_bytes"]) <= 1
+
+
+def test_trace_summary_cuts_workloads_at_their_clock_probes(tmp_path, capsys):
+    # Two workloads of the bench: A's 5 + 3 + 3 calls around its 2 probes, then
+    # B, whose first kernel A never launched. A torch fill is left out.
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X"]
+    rows, t = [], 0
+
+    def add(name, dur_ns, grid=256 * 4):
+        nonlocal t
+        rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur_ns,
+                     "Grid_Size_X": grid, "Workgroup_Size_X": 256})
+        t += dur_ns + 100
+
+    A = "void mxfa::(anonymous namespace)::fwd_bf16_kernel<128, 0>(mxfa::FwdParams)"
+    P = "mxfa::(anonymous namespace)::clock_probe_kernel(unsigned long long*, unsigned int)"
+    B = "void mxfa::(anonymous namespace)::decode_split_kernel<false, false, false>(mxfa::DecodeParams)"
+    for _ in range(5):
+        add(A, 90_000)
+    for _ in range(2):
+        for _ in range(3):
+            add(A, 80_000)
+        add(P, 1_000_000, grid=64)
+    add("void at::native::vectorized_elementwise_kernel<4>(int)", 2_000)
+    for d in (70_000, 71_000, 72_000):
+        add(A, d)
+    for _ in range(4):
+        add(B, 200_000)
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        w.writerows(rows)
+    bench.trace_summarize(str(path), ["wa", "wb"], tail=3, probes=2)
+    out = capsys.readouterr().out.splitlines()
+    body = [l for l in out[2:] if l.startswith("|")]
+    assert len(body) == 2
+    assert body[0].startswith("| wa | `fwd_bf16_kernel<128, 0>` | 4 | 14 |")
+    assert "| 71.0 | 70.0 | 72.0 |" in body[0]  # median / min / max of the last three calls, us
+    assert body[1].startswith("| wb | `decode_split_kernel<false, false, false>` | 4 | 4 |")
