@@ -98,11 +98,12 @@ def test_varlen_matches_oracle(case):
 
 
 def test_varlen_work_list_many_segments_dirty_workspace():
-    """The work list: more segments than one pass of its scan (1500), empty q and k
-    segments, a workspace full of garbage beforehand, then a smaller problem in the
+    """The work list: more segments than its LDS holds (2500: lengths and prefix sums
+    read from global memory), more than one pass of its scan (1500), empty q and k
+    segments, a workspace full of garbage beforehand, then smaller problems in the
     same workspace -- every row against the oracle."""
     rng = np.random.RandomState(2600)
-    for rep, batch in enumerate((1500, 37)):
+    for rep, batch in enumerate((2500, 1500, 37)):
         lq = [int(x) for x in rng.randint(0, 70, batch)]
         lk = [int(q + rng.randint(-5, 40)) if q else int(rng.randint(0, 3)) for q in lq]
         lk = [max(0, x) for x in lk]

@@ -22,7 +22,9 @@ namespace mxfa {
 namespace {
 
 constexpr int kThreads = 1024;
-constexpr int kBuckets = 1024;  // work is bucketed as min(kBuckets - 1, tiles >> shift)
+constexpr int kWaves = kThreads / 64;
+constexpr int kBuckets = 1024;   // work is bucketed as min(kBuckets - 1, tiles >> shift)
+constexpr int kLdsBatch = 2048;  // up to this many segments, their lengths and prefix sums stay in LDS
 
 // Key tiles of width bn that q tile t (rows [t*bm, t*bm + bm)) of a segment
 // with sq queries and sk keys streams; 0 when no row sees a key.
@@ -38,7 +40,8 @@ MXFA_DEV int tile_work(int t, int sq, int sk, int bm, int bn, int causal, int wl
 
 // Segment of item i: the last b with prefix[b] <= i (prefix non-decreasing,
 // prefix[0] = 0 <= i < prefix[batch]).
-MXFA_DEV int find_segment(const int* prefix, int batch, int i) {
+template <typename Ptr>
+MXFA_DEV int find_segment(Ptr prefix, int batch, int i) {
     int lo = 0, hi = batch - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -48,27 +51,44 @@ MXFA_DEV int find_segment(const int* prefix, int batch, int i) {
     return lo;
 }
 
-// Inclusive sum over the work group of one value per thread (LDS scan);
-// *total gets the sum over all threads.
-MXFA_DEV int block_inclusive_scan(int x, int* sbuf, int* total) {
-    const int tid = threadIdx.x;
-    sbuf[tid] = x;
-    __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const int y = tid >= d ? sbuf[tid - d] : 0;
-        __syncthreads();
-        sbuf[tid] += y;
-        __syncthreads();
+// Inclusive sum over the work group of one value per thread: a scan inside
+// each wave (lane shuffles), then over the 16 wave totals; *total gets the
+// sum over all threads. swave: kWaves ints of LDS.
+MXFA_DEV int block_inclusive_scan(int x, int* swave, int* total) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
     }
-    const int r = sbuf[tid];
-    *total = sbuf[kThreads - 1];
+    if (lane == 63) swave[w] = x;
     __syncthreads();
+    if (w == 0) {
+        int v = lane < kWaves ? swave[lane] : 0;
+#pragma unroll
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int y = __shfl_up(v, d, 64);
+            if (lane >= d) v += y;
+        }
+        if (lane < kWaves) swave[lane] = v;
+    }
+    __syncthreads();
+    const int r = x + (w > 0 ? swave[w - 1] : 0);
+    *total = swave[kWaves - 1];
+    __syncthreads();  // swave is reused by the next scan
     return r;
 }
 
+// kLds: the segments' lengths and prefix sums in LDS (batch <= kLdsBatch);
+// otherwise read from global memory.
+template <bool kLds>
 __global__ __launch_bounds__(kThreads) void varlen_worklist_kernel(const WorkListParams p) {
-    __shared__ int sbuf[kThreads];
+    __shared__ int swave[kWaves];
     __shared__ int hist[kBuckets];
+    __shared__ int s_prefix[kLds ? kLdsBatch + 1 : 1];
+    __shared__ int s_sq[kLds ? kLdsBatch : 1];
+    __shared__ int s_sk[kLds ? kLdsBatch : 1];
     const int tid = threadIdx.x;
     int* const ws = p.ws;
     int* const prefix = ws + 4;
@@ -76,34 +96,57 @@ __global__ __launch_bounds__(kThreads) void varlen_worklist_kernel(const WorkLis
 
     // q-tile counts of the segments -> exclusive prefix sums.
     int running = 0;
-    if (tid == 0) prefix[0] = 0;
+    if (tid == 0) {
+        prefix[0] = 0;
+        if constexpr (kLds) s_prefix[0] = 0;
+    }
     for (int b0 = 0; b0 < p.batch; b0 += kThreads) {
         const int b = b0 + tid;
         int nt = 0;
         if (b < p.batch) {
             const int sq = p.cu_q[b + 1] - p.cu_q[b];
             nt = (sq + p.bm - 1) / p.bm;
+            if constexpr (kLds) {
+                s_sq[b] = sq;
+                s_sk[b] = p.cu_k[b + 1] - p.cu_k[b];
+            }
         }
         int chunk = 0;
-        const int incl = block_inclusive_scan(nt, sbuf, &chunk);
-        if (b < p.batch) prefix[b + 1] = running + incl;
+        const int incl = block_inclusive_scan(nt, swave, &chunk);
+        if (b < p.batch) {
+            prefix[b + 1] = running + incl;
+            if constexpr (kLds) s_prefix[b + 1] = running + incl;
+        }
         running += chunk;
     }
     const int total = running;
     for (int i = tid; i < kBuckets; i += kThreads) hist[i] = 0;
-    // prefix[] lives in global memory and is read back by every thread
-    // below: a device-scope fence (write back, then invalidate this CU's L1)
-    // before the barrier, so no stale cached line is read.
-    __threadfence();
+    if constexpr (!kLds) {
+        // prefix[] lives in global memory and is read back by every thread
+        // below: a device-scope fence (write back, then invalidate this CU's
+        // L1) before the barrier, so no stale cached line is read.
+        __threadfence();
+    }
     __syncthreads();
+
+    auto item_work = [&](int i, int& b, int& t) {
+        if constexpr (kLds) {
+            b = find_segment(s_prefix, p.batch, i);
+            t = i - s_prefix[b];
+            return tile_work(t, s_sq[b], s_sk[b], p.bm, p.bn, p.causal, p.window_left, p.window_right);
+        } else {
+            b = find_segment(prefix, p.batch, i);
+            t = i - prefix[b];
+            const int sq = p.cu_q[b + 1] - p.cu_q[b];
+            const int sk = p.cu_k[b + 1] - p.cu_k[b];
+            return tile_work(t, sq, sk, p.bm, p.bn, p.causal, p.window_left, p.window_right);
+        }
+    };
 
     // Histogram of the items' work.
     for (int i = tid; i < total; i += kThreads) {
-        const int b = find_segment(prefix, p.batch, i);
-        const int t = i - prefix[b];
-        const int sq = p.cu_q[b + 1] - p.cu_q[b];
-        const int sk = p.cu_k[b + 1] - p.cu_k[b];
-        const int w = tile_work(t, sq, sk, p.bm, p.bn, p.causal, p.window_left, p.window_right);
+        int b, t;
+        const int w = item_work(i, b, t);
         atomicAdd(&hist[min(kBuckets - 1, w >> p.shift)], 1);
     }
     __syncthreads();
@@ -111,18 +154,15 @@ __global__ __launch_bounds__(kThreads) void varlen_worklist_kernel(const WorkLis
     // Start of each bucket, the heaviest bucket first.
     const int hb = hist[kBuckets - 1 - tid];
     int all = 0;
-    const int incl = block_inclusive_scan(hb, sbuf, &all);
+    const int incl = block_inclusive_scan(hb, swave, &all);
     hist[kBuckets - 1 - tid] = incl - hb;
     __syncthreads();
 
     // Scatter (segment, q tile) into its bucket's range (order inside a bucket
     // is arbitrary: every item is computed independently of where it runs).
     for (int i = tid; i < total; i += kThreads) {
-        const int b = find_segment(prefix, p.batch, i);
-        const int t = i - prefix[b];
-        const int sq = p.cu_q[b + 1] - p.cu_q[b];
-        const int sk = p.cu_k[b + 1] - p.cu_k[b];
-        const int w = tile_work(t, sq, sk, p.bm, p.bn, p.causal, p.window_left, p.window_right);
+        int b, t;
+        const int w = item_work(i, b, t);
         const int pos = atomicAdd(&hist[min(kBuckets - 1, w >> p.shift)], 1);
         // Only a segment longer than the max_seqlen_q the list was sized
         // for makes more items than the workspace holds: the lightest are
@@ -146,7 +186,10 @@ hipError_t launch_varlen_worklist(const WorkListParams& args, hipStream_t stream
     int shift = 0;
     while ((max_w >> shift) >= kBuckets) ++shift;
     p.shift = shift;
-    hipLaunchKernelGGL(varlen_worklist_kernel, dim3(1), dim3(kThreads), 0, stream, p);
+    if (p.batch <= kLdsBatch)
+        hipLaunchKernelGGL(varlen_worklist_kernel<true>, dim3(1), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(varlen_worklist_kernel<false>, dim3(1), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
