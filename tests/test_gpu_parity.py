@@ -846,3 +846,109 @@ def test_full_mla_decode_fp8():
 
     # Every one of the 512 x 16 rows, in one oracle call (the cache is dequantised once per call).
     _oracle_all_rows("mla_decode_fp8", "bf16", o_c, lse_c, run_rows, o_c.shape[0], w.heads_q, o_c.shape[0])
+
+
+# ------------------------------------------------ offsets past 4 GiB
+#
+# Segments whose K/V (or latent rows, or cache pages) start more than 2^32
+# bytes into their tensors: the visible keys are a small seeded problem placed
+# at the end of a long, zero-filled sequence, so that the oracle runs on the
+# small problem alone (with bottom-right alignment and a left window, the
+# query of the long sequence sees exactly the last 256 keys in both).
+
+def _embed_tail(small_rows, total_rows, tail_len, head_rows):
+    """A [total_rows, ...] zero GPU tensor: small_rows[:tail_len] at the end of the
+    first sequence (ending at head_rows), the rest right after it."""
+    d = dev()
+    big = torch.zeros((total_rows,) + tuple(small_rows.shape[1:]), dtype=small_rows.dtype, device=d)
+    big[head_rows - tail_len:head_rows] = small_rows[:tail_len].to(d)
+    big[head_rows:] = small_rows[tail_len:].to(d)
+    return big
+
+
+def test_prefill_offsets_past_4gib():
+    long_k = 17_000_000  # 256 B of K per key: the second segment starts 4.35 GB in
+    lq, lk = [1, 300], [256, 300]
+    p = workloads.make_problem(3900, dtype="bf16", heads_q=2, heads_kv=1, d_qk=128, d_v=128, lens_q=lq, lens_k=lk)
+    d = dev()
+    print("[prefill] offsets past 4 GiB", flush=True)
+    k = _embed_tail(p["k"], long_k + 300, 256, long_k)
+    v = _embed_tail(p["v"], long_k + 300, 256, long_k)
+    cq = p["cu_seqlens_q"].to(d)
+    ck = torch.tensor([0, long_k, long_k + 300], dtype=torch.int32, device=d)
+    scale = 128 ** -0.5
+    o, lse = mx.mxfa_fwd_varlen(p["q"].to(d), k, v, cq, ck, 300, long_k, causal=True, window=(255, 0),
+                                scale=scale)
+    torch.cuda.synchronize()
+    o_g, lse_g = o.float().cpu().numpy(), lse.cpu().numpy()
+    del k, v, o, lse
+    torch.cuda.empty_cache()
+    o_ref, lse_ref, _ = oracle_varlen(p, causal=True, window=(255, 0), softcap=0.0, scale=scale)
+    compare(o_g.reshape(-1, 128), lse_g.T.reshape(-1), o_ref.reshape(-1, 128), lse_ref.reshape(-1), "bf16",
+            "prefill past 4 GiB")
+
+
+def test_latent_decode_offsets_past_4gib():
+    long_k = 3_800_000  # 1152 B per latent row: the second sequence starts 4.38 GB in
+    lq, lk = [1, 4], [256, 300]
+    p = workloads.make_problem(3910, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    d = dev()
+    print("[decode] offsets past 4 GiB", flush=True)
+    scale = 1.0 / math.sqrt(576)
+    kv = _embed_tail(p["kv"], long_k + 300, 256, long_k)
+    cq = p["cu_seqlens_q"].to(d)
+    ck = torch.tensor([0, long_k, long_k + 300], dtype=torch.int32, device=d)
+    o, lse = mx.mxfa_decode_splitkv(p["q"].to(d), kv, cq, ck, 4, long_k, head_dim_v=512, causal=True,
+                                    window=(255, 0), scale=scale)
+    torch.cuda.synchronize()
+    o_g, lse_g = o.float().cpu().numpy(), lse.cpu().numpy()
+    del kv, o, lse
+    torch.cuda.empty_cache()
+    import oracle
+
+    kvn = to_np(p["kv"])
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kvn, kvn[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), causal=True, window=(255, 0), scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            "latent decode past 4 GiB")
+
+
+def test_paged_decode_pages_past_4gib():
+    # 60,000 pages of 64 latent rows (73,728 B each): the visible pages of both
+    # sequences lie past page 58,255, i.e. more than 2^32 bytes into the cache.
+    page, num_pages, long_k = 64, 60_000, 3_800_000
+    lq, lk = [1, 4], [256, 300]
+    p = workloads.make_problem(3920, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=lq,
+                               lens_k=lk, shared_kv=True)
+    d = dev()
+    print("[paged] pages past 4 GiB", flush=True)
+    scale = 1.0 / math.sqrt(576)
+    cache = torch.zeros((num_pages, page, 1, 576), dtype=torch.bfloat16, device=d)
+    max_pages = long_k // page
+    table = torch.zeros((2, max_pages), dtype=torch.int32)
+    # sequence 0: its last 4 logical pages hold the small problem's 256 keys
+    for i in range(4):
+        phys = 59_990 + i
+        table[0, max_pages - 4 + i] = phys
+        cache[phys] = p["kv"][i * page:(i + 1) * page].to(d)
+    # sequence 1: 300 keys in 5 pages
+    for i in range(5):
+        phys = 59_995 + i
+        table[1, i] = phys
+        rows = p["kv"][256 + i * page:min(556, 256 + (i + 1) * page)]
+        cache[phys, :rows.shape[0]] = rows.to(d)
+    seqlens = torch.tensor([long_k, 300], dtype=torch.int32, device=d)
+    o, lse = mx.mxfa_decode_splitkv_paged(p["q"].to(d), cache, p["cu_seqlens_q"].to(d), seqlens, table.to(d), 4,
+                                          long_k, head_dim_v=512, causal=True, window=(255, 0), scale=scale)
+    torch.cuda.synchronize()
+    o_g, lse_g = o.float().cpu().numpy(), lse.cpu().numpy()
+    del cache, o, lse
+    torch.cuda.empty_cache()
+    import oracle
+
+    kvn = to_np(p["kv"])
+    o_ref, lse_ref, _ = oracle.attention_rows(to_np(p["q"]), kvn, kvn[:, :, :512], p["cu_seqlens_q"].numpy(),
+                                              p["cu_seqlens_k"].numpy(), causal=True, window=(255, 0), scale=scale)
+    compare(o_g.reshape(-1, 512), lse_g.T.reshape(-1), o_ref.reshape(-1, 512), lse_ref.reshape(-1), "bf16",
+            "paged decode past 4 GiB")
