@@ -538,23 +538,41 @@ void fwd_bf16_kernel(const FwdParams p) {
 
     // Epilogue: combine the two lane halves' sums, normalise, store. O is
     // divided by the sum of the bf16 weights the P V MFMAs multiplied (so
-    // the weights of a row sum to one), the LSE takes the fp32 sum.
+    // the weights of a row sum to one), the LSE takes the fp32 sum. O goes
+    // through this wave's own part of the K/V buffers (free after the last
+    // step's barrier; chunks XOR-swizzled by row), so that every global store
+    // writes whole rows: 64 lanes x 16 bytes = 4 rows of 256 bytes (d = 128)
+    // or 8 of 128 (d = 64), instead of 16 bytes of each of 32 rows.
     const float l_row = half_sum(l_part);
     const float lb_row = half_sum(lb_part);
-    if (!q_valid) return;
     const float inv = (lb_row > 0.0f) ? 1.0f / lb_row : 0.0f;
-    uint16_t* O = static_cast<uint16_t*>(p.o) + (long long)(q_start + qi) * q_tok + (long long)h * D;
+    {
+        typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
+        typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+        constexpr int OCH = D / 8;      // 16-byte chunks per O row
+        constexpr int RPI = 64 / OCH;   // rows per store instruction
+        char* const ost = wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+        for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-            const int d = db * 32 + 8 * rg + 4 * lh;
-            const u32x2_t v = {pack_bf16x2(acc[db][4 * rg + 0] * inv, acc[db][4 * rg + 1] * inv),
-                               pack_bf16x2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv)};
-            store_u32x2(O + d, v);
+            for (int rg = 0; rg < 4; ++rg) {
+                const int c = db * 4 + rg;  // channels 8c .. 8c+7; this lane holds 8c + 4*lh .. +3
+                const u32x2_t v = {pack_bf16x2(acc[db][4 * rg + 0] * inv, acc[db][4 * rg + 1] * inv),
+                                   pack_bf16x2(acc[db][4 * rg + 2] * inv, acc[db][4 * rg + 3] * inv)};
+                *(lds_u32x2*)to_lds(ost + lr * ROWB + ((c ^ (lr % OCH)) << 4) + lh * 8) = v;
+            }
+        }
+        const int rsub = lane / OCH;
+        const int c = lane % OCH;
+        uint16_t* const Ow = static_cast<uint16_t*>(p.o) + (long long)(q_start + wrow0) * q_tok + (long long)h * D;
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int r = it * RPI + rsub;  // row of this wave's 32
+            const u32x4_t v = *(const lds_u32x4*)to_lds(ost + r * ROWB + ((c ^ (r % OCH)) << 4));
+            if (wrow0 + r < sq) store_u32x4(Ow + (long long)r * q_tok + c * 8, v);
         }
     }
-    if (p.lse && lh == 0) {
+    if (p.lse && lh == 0 && q_valid) {
         const float lse = (l_row > 0.0f) ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
         const long long idx = p.cu_q ? (long long)h * p.total_q + q_start + qi
                                      : ((long long)b * p.heads_q + h) * sq + qi;
