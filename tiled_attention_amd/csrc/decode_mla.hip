@@ -76,6 +76,10 @@ void decode_split_kernel(const DecodeParams p) {
     __shared__ __attribute__((aligned(1024))) char sT2[TILEB];
     __shared__ __attribute__((aligned(1024))) char sT3[TILEB];
     __shared__ __attribute__((aligned(1024))) f32x4_t sS[4][4][64];  // partial S^T per wave: [wave][r/4][lane]
+    // fp8: a second exchange buffer (tiles alternate between the two), which
+    // the three-stage fp8 pipeline leaves room for.
+    __shared__ __attribute__((aligned(1024))) f32x4_t sS1[4][4][64];
+    typedef f32x4_t Exchange[4][4][64];
 
     int id = blockIdx.x;
     const int sp = id % p.splits;
@@ -228,7 +232,7 @@ void decode_split_kernel(const DecodeParams p) {
         issue_part(tile_rsrc(kt, page_of(kt)), stage, 0, LOADS);
     };
     // fp8 rows take another way into LDS: 16-byte chunks (16 values) are
-    // loaded into registers four tiles ahead, converted to bf16 (exact: every
+    // loaded into registers three tiles ahead, converted to bf16 (exact: every
     // e4m3 value is a bf16 value) and written into the same swizzled bf16
     // stages. Chunk P = n*256 + tid of a tile is row P / 36, chunk P % 36,
     // whose values are the bf16 logical chunks 2c and 2c + 1 of the row (at
@@ -254,6 +258,10 @@ void decode_split_kernel(const DecodeParams p) {
         const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt, 0);
 #pragma unroll
         for (int n = 0; n < LOADS8; ++n) r.v[n] = buffer_load16(rs, go8[n], 0);
+    };
+    auto load8_part = [&](const __amdgpu_buffer_rsrc_t& rs, Raw8& r, int n0, int n1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = n0; n < n1; ++n) r.v[n] = buffer_load16(rs, go8[n], 0);
     };
     auto store8 = [&](const Raw8& r, char* stage) __attribute__((always_inline)) {
 #pragma unroll
@@ -326,14 +334,14 @@ void decode_split_kernel(const DecodeParams p) {
     // the current tile; the partner's are added here. Same arithmetic as
     // softmax_tile.
     auto qk_softmax = [&](const char* tile, const f32x16_t& s_cur, int kt, uint32_t (&pk)[8], float& alpha,
-                          auto&& mid_hook) __attribute__((always_inline)) -> f32x16_t {
+                          const Exchange& xs, auto&& mid_hook) __attribute__((always_inline)) -> f32x16_t {
         uint32_t kxl[4] = {kx[0], kx[1], kx[2], kx[3]};
         asm volatile("" : "+v"(kxl[0]), "+v"(kxl[1]), "+v"(kxl[2]), "+v"(kxl[3]));
         constexpr int AHEAD = 6;  // K reads in flight ahead of their MFMA
         bf16x8_t kr[KSTEPS];
         f32x4_t po[4];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) po[q4] = sS[w ^ 2][q4][lane];
+        for (int q4 = 0; q4 < 4; ++q4) po[q4] = xs[w ^ 2][q4][lane];
 #pragma unroll
         for (int ks = 0; ks < AHEAD; ++ks)
             kr[ks] = __builtin_bit_cast(bf16x8_t, lds_read16(tile + kxl[ks & 3] + 128 * (ks >> 2)));
@@ -426,16 +434,66 @@ void decode_split_kernel(const DecodeParams p) {
         __builtin_amdgcn_sched_group_barrier(0x008, PV_AHEAD, 0);
     };
 
+    // fp8: O^T += V^T P^T as pv_tile, with the conversion of a loaded tile
+    // into its stage spread over the MFMAs: after MFMA m (2 <= m < 12) the
+    // four conversions and the LDS write of half chunk m - 2 (chunk (m-2)/2,
+    // its first or second 8 values), fenced so that the write issues while
+    // the MFMA runs. A thread with no fifth chunk reloaded its first one,
+    // so it rewrites the same values to the same place.
+    auto pv_fill = [&](const char* tile, const uint32_t (&pk)[8], const Raw8& r, char* stage)
+                       __attribute__((always_inline)) {
+        uint32_t vxl[4] = {vx[0][0], vx[0][1], vx[1][0], vx[1][1]};
+        asm volatile("" : "+v"(vxl[0]), "+v"(vxl[1]), "+v"(vxl[2]), "+v"(vxl[3]));
+        constexpr int NM = 2 * CBLK;  // MFMAs: m = CBLK*h + cb
+        constexpr int AHEAD = 4;
+        u32x2_t ra[NM], rb2[NM];
+        auto rd = [&](int m) __attribute__((always_inline)) {
+            const int h = m / CBLK;
+            const int cb = m % CBLK;
+            const char* base = tile + 16 * ROWB * h + 128 * (cb >> 1);
+            ra[m] = lds_read_tr16(base + vxl[cb & 1]);
+            rb2[m] = lds_read_tr16(base + vxl[2 + (cb & 1)]);
+        };
+#pragma unroll
+        for (int m = 0; m < AHEAD; ++m) rd(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m + AHEAD < NM) rd(m + AHEAD);
+            const int h = m / CBLK;
+            const int cb = m % CBLK;
+            const u32x4_t pv = {pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
+            const u32x4_t av = {ra[m][0], ra[m][1], rb2[m][0], rb2[m][1]};
+            acc[cb] = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, pv), acc[cb]);
+            if (m >= 2 && m < 2 + 2 * LOADS8) {
+                const int n = (m - 2) >> 1;
+                const int half = (m - 2) & 1;
+                uint32_t hv[4];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int wd = 2 * half + k;
+                    hv[2 * k] = __builtin_bit_cast(uint32_t,
+                                                   __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[n][wd], 1.0f, false));
+                    hv[2 * k + 1] = __builtin_bit_cast(
+                        uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)r.v[n][wd], 1.0f, true));
+                }
+                typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+                *(lds_u32x4*)to_lds(stage + (lo8[n] ^ (16u * half))) = u32x4_t{hv[0], hv[1], hv[2], hv[3]};
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     if (lo <= hi) {
         const int kt0 = lo & ~(BN - 1);
         const int ntiles = (hi - kt0) / BN + 1;
         // Tile j lives in stage j % 4. Past the end, tiles are issued as
         // zero-byte loads, so the count of loads behind each wait is fixed.
         f32x16_t s_mine = f32x16_t{};
-        auto publish = [&]() __attribute__((always_inline)) {
+        auto publish = [&](Exchange& xs) __attribute__((always_inline)) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4)
-                sS[w][q4][lane] = f32x4_t{s_mine[4 * q4], s_mine[4 * q4 + 1], s_mine[4 * q4 + 2], s_mine[4 * q4 + 3]};
+                xs[w][q4][lane] = f32x4_t{s_mine[4 * q4], s_mine[4 * q4 + 1], s_mine[4 * q4 + 2], s_mine[4 * q4 + 3]};
         };
       if constexpr (!kFp8) {
         issue_tile(kt0, sT0);
@@ -445,7 +503,7 @@ void decode_split_kernel(const DecodeParams p) {
         asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's loads of tile 0
         lds_barrier();
         s_mine = qk_tile(sT0);
-        publish();
+        publish(sS);
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // this wave's loads of tile 1
         lds_barrier();
         // Step j: add the partner's partial scores of tile j; compute this
@@ -478,11 +536,11 @@ void decode_split_kernel(const DecodeParams p) {
             // compiler then keeps an exact count of the LDS reads in flight.
             // On the last step the scores are of a finished (zero-filled)
             // tile and are not used.
-            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha,
+            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, sS,
                                 [&]() __attribute__((always_inline)) { issue_part(rfill, prv, 3, 6); });
             lds_barrier();
             issue_part(rfill, prv, 6, LOADS);
-            publish();
+            publish(sS);
             if (wave_any(alpha != 1.0f)) {
 #pragma unroll
                 for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
@@ -510,9 +568,9 @@ void decode_split_kernel(const DecodeParams p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
         // fp8 rows: tile j is loaded into registers in step j-3 (set j % 3)
-        // and converted into its LDS stage j % 3 at the end of step j-2: two
-        // steps of load latency covered with three register sets (a fourth
-        // set left too few registers for the P V reads to run ahead).
+        // and converted into its LDS stage j % 3 during the P V MFMAs of step
+        // j-2: two steps of load latency covered with three register sets (a
+        // fourth set left too few registers for the P V reads to run ahead).
         Raw8 R0, R1, R2;
         load8(kt0, R0);
         load8(kt0 + BN, R1);
@@ -521,12 +579,16 @@ void decode_split_kernel(const DecodeParams p) {
         store8(R1, sT1);
         lds_barrier();
         s_mine = qk_tile(sT0);
-        publish();
+        publish(sS);
         lds_barrier();
         // Step j: loads of tile j+3 into the registers of tile j (converted
-        // at the end of step j-2); scores of tile j+1 with the softmax of tile
-        // j; barrier; publish, P V of tile j; tile j+2 converted into the
-        // stage of tile j-1 (last read in step j-1); barrier.
+        // in step j-2), in three parts; scores of tile j+1 with the softmax
+        // of tile j; publish; P V of tile j with tile j+2 converted into the
+        // stage of tile j-1 (last read in step j-1); barrier. The partial
+        // scores of tile t go through exchange buffer t % 2: publishing tile
+        // j+1's in step j overwrites tile j-1's, which the partner read in
+        // step j-1, before the barrier that ended it; so one barrier per step
+        // suffices.
         auto step8 = [&](auto stage_tag, int j, Raw8& rl, const Raw8& rc) __attribute__((always_inline)) {
             constexpr int S = decltype(stage_tag)::value;
             char* const cur = S == 0 ? sT0 : S == 1 ? sT1 : sT2;
@@ -534,16 +596,17 @@ void decode_split_kernel(const DecodeParams p) {
             char* const fill = S == 0 ? sT2 : S == 1 ? sT0 : sT1;
             uint32_t pk[8];
             float alpha = 1.0f;
-            load8(kt0 + (j + 3) * BN, rl);
-            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, []() __attribute__((always_inline)) {});
-            lds_barrier();
-            publish();
+            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt0 + (j + 3) * BN, 0);
+            load8_part(rs, rl, 0, 2);
+            s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, (j & 1) ? sS1 : sS,
+                                [&]() __attribute__((always_inline)) { load8_part(rs, rl, 2, 4); });
+            load8_part(rs, rl, 4, LOADS8);
+            publish((j & 1) ? sS : sS1);
             if (wave_any(alpha != 1.0f)) {
 #pragma unroll
                 for (int cb = 0; cb < CBLK; ++cb) acc[cb] *= alpha;
             }
-            pv_tile(cur, pk);
-            store8(rc, fill);
+            pv_fill(cur, pk, rc, fill);
             lds_barrier();
         };
         using st0 = std::integral_constant<int, 0>;
