@@ -124,7 +124,7 @@ def attention_rows(q, k, v, cu_q, cu_k, *, causal=False, window=(-1, -1), softca
     dv = v.shape[2]
     if k.shape[2] != dqk or v.shape[0] != k.shape[0] or v.shape[1] != hkv:
         raise ValueError("inconsistent q/k/v shapes")
-    if v.strides[2] != v.itemsize:
+    if v.size and v.strides[2] != v.itemsize:  # (an empty array's strides may all be 0)
         raise ValueError("v's last dimension must be contiguous")
     batch = len(cu_q) - 1
     if len(cu_k) != batch + 1:

@@ -314,6 +314,15 @@ def test_shared_kv_view_equals_copy():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_problem_with_no_tokens():
+    """A packed problem whose segments hold no queries and no keys (the empty
+    arrays torch hands over may carry strides that describe no layout)."""
+    p = workloads.make_problem(58, dtype="bf16", heads_q=16, heads_kv=4, d_qk=64, d_v=64, lens_q=[0], lens_k=[0])
+    q, k, v = (t.float().numpy() for t in (p["q"], p["k"], p["v"]))
+    o, lse, _ = oracle.attention_rows(q, k, v, p["cu_seqlens_q"].numpy(), p["cu_seqlens_k"].numpy())
+    assert o.shape == (0, 16, 64) and lse.shape == (0, 16)
+
+
 def test_row_selection_matches_full():
     q, k, v, cq, ck = _problem(57, "bf16", 4, 2, 16, 16, [10, 20], [10, 25])
     o, lse, _ = oracle.attention_rows(q, k, v, cq, ck, causal=True)
