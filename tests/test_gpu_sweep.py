@@ -74,7 +74,7 @@ def _prefill_case(i):
                 window=window, cap=cap, scale=_scale(rng, d))
 
 
-PREFILL = [_prefill_case(i) for i in range(24)]
+PREFILL = [_prefill_case(i) for i in range(64)]
 
 
 @pytest.mark.parametrize("c", PREFILL, ids=[f"prefill{i}" for i in range(len(PREFILL))])
@@ -103,7 +103,7 @@ def _dense_case(i):
                 window=window, cap=cap, scale=_scale(rng, d))
 
 
-DENSE = [_dense_case(i) for i in range(12)]
+DENSE = [_dense_case(i) for i in range(32)]
 
 
 @pytest.mark.parametrize("c", DENSE, ids=[f"dense{i}" for i in range(len(DENSE))])
@@ -148,9 +148,9 @@ def _latent_case(i, base):
                 cap=cap, splits=splits, scale=_scale(rng, 576), page=int(rng.choice([32, 64, 128, 256])))
 
 
-LATENT = [_latent_case(i, 43_000) for i in range(10)]
-LATENT_FP8 = [_latent_case(i, 44_000) for i in range(6)]
-LATENT_PAGED = [_latent_case(i, 45_000) for i in range(6)]
+LATENT = [_latent_case(i, 43_000) for i in range(24)]
+LATENT_FP8 = [_latent_case(i, 44_000) for i in range(16)]
+LATENT_PAGED = [_latent_case(i, 45_000) for i in range(16)]
 
 
 def _latent_problem(c):
@@ -235,7 +235,7 @@ def _gqa_case(i):
                 cap=cap, splits=splits, scale=_scale(rng, d))
 
 
-GQA = [_gqa_case(i) for i in range(12)]
+GQA = [_gqa_case(i) for i in range(32)]
 
 
 @pytest.mark.parametrize("c", GQA, ids=[f"gqa{i}" for i in range(len(GQA))])
