@@ -205,11 +205,17 @@ void fwd_bf16_kernel(const FwdParams p) {
         if (kt >= sk) bytes = 0;  // a tile wholly past the end is a zero-byte load
         return (uint32_t)(bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
     };
-    // One tile into LDS: LOADS loads per thread.
-    auto issue = [&](const uint16_t* seg, int kt, char* tile) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(seg + (long long)kt * kv_tok, tile_bytes(kt));
+    // This wave's part of a tile in LDS as a wave-uniform byte offset: each
+    // load's LDS address (M0) is then a scalar sum instead of a lane read.
+    const uint32_t woff = __builtin_amdgcn_readfirstlane((uint32_t)(wave * 64 * 16));
+    // One tile into LDS: LOADS loads per thread, reading `bytes` from key kt on.
+    auto issue_b = [&](const uint16_t* seg, int kt, char* tile, uint32_t bytes) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(seg + (long long)kt * kv_tok, bytes);
 #pragma unroll
-        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, tile + (n * NTHREADS + wave * 64) * 16, goff, n * gstep);
+        for (int n = 0; n < LOADS; ++n) buffer_load_lds16(r, tile + n * NTHREADS * 16 + woff, goff, n * gstep);
+    };
+    auto issue = [&](const uint16_t* seg, int kt, char* tile) __attribute__((always_inline)) {
+        issue_b(seg, kt, tile, tile_bytes(kt));
     };
 
     f32x16_t acc[DBLK];
@@ -456,6 +462,15 @@ void fwd_bf16_kernel(const FwdParams p) {
     if (kv_lo <= kv_hi) {
         const int kt0 = kv_lo & ~(BN - 1);
         const int ntiles = (kv_hi - kt0) / BN + 1;
+        // The loop's loads read one tile's span, or for the last tile up to the
+        // segment's end (rows past it read as zero); both are set here, so
+        // the per-step issue is a compare, a select and scalar adds (the
+        // 64-bit range arithmetic per tile took ~2% of the prefill's time).
+        const long long span64 = (long long)(BN - 1) * kv_tok * 2 + D * 2;
+        const uint32_t span = (uint32_t)(span64 > 0x7fffffffLL ? 0x7fffffffLL : span64);
+        const int kt_last = kt0 + (ntiles - 1) * BN;
+        const uint32_t last_bytes = min(span, tile_bytes(kt_last));
+        auto loop_bytes = [&](int kt) __attribute__((always_inline)) { return kt == kt_last ? last_bytes : span; };
         // Prologue: K0, V0, K1 in flight; S and row max of tile 0.
         issue(Kseg, kt0, sK0);
         issue(Vseg, kt0, sV0);
@@ -496,8 +511,8 @@ void fwd_bf16_kernel(const FwdParams p) {
             // wait at this step's end then finds them landed more often than
             // when parts were issued inside the phases (3% faster on the
             // causal and chunked prefill workloads).
-            if (j + 2 < ntiles) issue(Kseg, kt + 2 * BN, k_fill);
-            if (j + 1 < ntiles) issue(Vseg, kt + BN, v_fill);
+            if (j + 2 < ntiles) issue_b(Kseg, kt + 2 * BN, k_fill, loop_bytes(kt + 2 * BN));
+            if (j + 1 < ntiles) issue_b(Vseg, kt + BN, v_fill, loop_bytes(kt + BN));
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
