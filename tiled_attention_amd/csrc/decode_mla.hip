@@ -487,6 +487,20 @@ void decode_split_kernel(const DecodeParams p) {
     if (lo <= hi) {
         const int kt0 = lo & ~(BN - 1);
         const int ntiles = (hi - kt0) / BN + 1;
+        // Contiguous cache: the loop's tiles read one tile's span, the last
+        // tile of the split up to the segment's end, tiles past the split
+        // nothing; the spans are set here so that a step's resource is a
+        // compare, two selects and the tile's base address.
+        const long long span64 = ((long long)(BN - 1) * kv_tok_stride + DQK) * ESZ;
+        const uint32_t span = (uint32_t)(span64 > 0x7fffffffLL ? 0x7fffffffLL : span64);
+        const int kt_last = kt0 + (ntiles - 1) * BN;
+        long long last64 = ((long long)(sk - kt_last - 1) * kv_tok_stride + DQK) * ESZ;
+        const uint32_t last_bytes = (uint32_t)(last64 < (long long)span ? last64 : (long long)span);
+        auto loop_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+            if constexpr (kPaged) return tile_rsrc(kt, phys);
+            const uint32_t bytes = kt > hi ? 0u : (kt == kt_last ? last_bytes : span);
+            return make_rsrc(bytes ? KVseg + (long long)kt * kv_tok_stride * ESZ : KVseg, bytes);
+        };
         // Tile j lives in stage j % 4. Past the end, tiles are issued as
         // zero-byte loads, so the count of loads behind each wait is fixed.
         f32x16_t s_mine = f32x16_t{};
@@ -523,7 +537,7 @@ void decode_split_kernel(const DecodeParams p) {
             const int kt_fill = kt0 + (j + 3) * BN;  // tile j+3 -> the stage of tile j-1
             uint32_t pk[8];
             float alpha = 1.0f;
-            const __amdgpu_buffer_rsrc_t rfill = tile_rsrc(kt_fill, phys_fill);
+            const __amdgpu_buffer_rsrc_t rfill = loop_rsrc(kt_fill, phys_fill);
             phys_fill = page_of(kt_fill + BN);
             // Wait for the page-table read here, where no LDS read is in
             // flight: the scalar load shares the LDS wait counter and returns
@@ -596,7 +610,7 @@ void decode_split_kernel(const DecodeParams p) {
             char* const fill = S == 0 ? sT2 : S == 1 ? sT0 : sT1;
             uint32_t pk[8];
             float alpha = 1.0f;
-            const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt0 + (j + 3) * BN, 0);
+            const __amdgpu_buffer_rsrc_t rs = loop_rsrc(kt0 + (j + 3) * BN, 0);
             load8_part(rs, rl, 0, 2);
             s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, (j & 1) ? sS1 : sS,
                                 [&]() __attribute__((always_inline)) { load8_part(rs, rl, 2, 4); });
