@@ -40,6 +40,9 @@
  *    must be 16-byte aligned; lse and cu_seqlens 4-byte aligned.
  *  - The contents of cu_seqlens (non-decreasing, starting at 0, last entry =
  *    total) are the caller's contract and are not checked on the device.
+ *  - heads_q and heads_kv are at most MXFA_MAX_HEADS; beyond it a call
+ *    returns MXFA_ERR_UNSUPPORTED (the kernels address one tile of keys, all
+ *    kv heads of each key row, through a buffer range of under 2 GiB).
  *
  * Errors
  * ------
@@ -60,10 +63,12 @@ extern "C" {
 
 typedef struct ihipStream_t* mxfa_stream_t; /* the same handle as hipStream_t */
 
+#define MXFA_MAX_HEADS 16384 /* largest heads_q and heads_kv any call accepts */
+
 typedef enum {
     MXFA_OK = 0,
     MXFA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, inconsistent heads, ... */
-    MXFA_ERR_UNSUPPORTED = 2, /* head dim or dtype the library has no kernel for */
+    MXFA_ERR_UNSUPPORTED = 2, /* head dim, dtype or head count the library has no kernel for */
     MXFA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query says */
     MXFA_ERR_HIP = 4          /* the HIP runtime reported an error (launch, device query) */
 } mxfa_status;

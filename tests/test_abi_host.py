@@ -106,7 +106,8 @@ def fwd(lib, **kw):
     (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID), (dict(batch=-1), INVALID),
     (dict(sq=-3), INVALID), (dict(q=None), INVALID), (dict(o=None), INVALID), (dict(k=None), INVALID),
     (dict(q=A + 2), INVALID), (dict(v=A + 8), INVALID), (dict(lse=A + 2), INVALID),
-    (dict(batch=1 << 20, sq=1 << 12), INVALID),
+    (dict(batch=1 << 20, sq=1 << 12), INVALID), (dict(hq=16386, hkv=2), UNSUPPORTED),
+    (dict(hq=32768, hkv=32768), UNSUPPORTED),
     (dict(batch=0), OK), (dict(sq=0), OK), (dict(batch=0, q=None, k=None, v=None, o=None), OK),
 ])
 def test_fwd_host_checks(lib, kw, status):
@@ -128,7 +129,8 @@ def varlen(lib, **kw):
 # cases because it is missing, too small or misaligned), or is an empty call.
 @pytest.mark.parametrize("kw,status", [
     (dict(cq=None), INVALID), (dict(ck=A + 2), INVALID), (dict(mq=30), INVALID), (dict(tk=-1), INVALID),
-    (dict(d=80), UNSUPPORTED), (dict(hq=3), INVALID), (dict(batch=0), OK), (dict(tq=0, mq=0), OK),
+    (dict(d=80), UNSUPPORTED), (dict(hq=3), INVALID), (dict(hq=32768, hkv=2), UNSUPPORTED), (dict(batch=0), OK),
+    (dict(tq=0, mq=0), OK),
     (dict(ws=None, ws_bytes=1 << 20), WORKSPACE), (dict(ws_bytes=15), WORKSPACE),
     (dict(ws=A + 8, ws_bytes=1 << 20), INVALID), (dict(batch=0, ws=None), OK),
 ])
@@ -162,7 +164,7 @@ def decode(lib, **kw):
     (dict(dqk=128, dv=128), UNSUPPORTED), (dict(dv=256), UNSUPPORTED), (dict(splits=65), INVALID),
     (dict(splits=-1), INVALID), (dict(ws=None), WORKSPACE), (dict(ws_bytes=1000), WORKSPACE),
     (dict(ws=A + 4), INVALID), (dict(kv=None), INVALID), (dict(hq=16, hkv=3), INVALID),
-    (dict(batch=0), OK),
+    (dict(hq=20000, hkv=1), UNSUPPORTED), (dict(batch=0), OK),
 ])
 def test_decode_host_checks(lib, kw, status):
     assert decode(lib, **kw) == status
@@ -231,7 +233,7 @@ def gqa(lib, **kw):
     (dict(splits=65), INVALID), (dict(splits=-1), INVALID), (dict(ws=None), WORKSPACE),
     (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 4), INVALID), (dict(k=None), INVALID),
     (dict(v=A + 2), INVALID), (dict(cq=None), INVALID), (dict(mq=3), INVALID), (dict(tk=-1), INVALID),
-    (dict(batch=0), OK), (dict(tq=0, mq=0), OK),
+    (dict(hq=32768, hkv=4), UNSUPPORTED), (dict(batch=0), OK), (dict(tq=0, mq=0), OK),
 ])
 def test_gqa_decode_host_checks(lib, kw, status):
     assert gqa(lib, **kw) == status

@@ -39,6 +39,9 @@ mxfa_status check_common(int heads_q, int heads_kv, int window_left, int window_
                          float scale) {
     if (heads_q < 1 || heads_kv < 1) return fail(MXFA_ERR_INVALID_ARG, "heads_q and heads_kv must be >= 1");
     if (heads_q % heads_kv) return fail(MXFA_ERR_INVALID_ARG, "heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+    if (heads_q > MXFA_MAX_HEADS || heads_kv > MXFA_MAX_HEADS)
+        return fail(MXFA_ERR_UNSUPPORTED, "heads_q (%d) and heads_kv (%d) must be at most %d", heads_q, heads_kv,
+                    MXFA_MAX_HEADS);
     if (window_left < -1 || window_right < -1) return fail(MXFA_ERR_INVALID_ARG, "window bounds must be >= -1");
     if (!isfinite(softcap) || softcap < 0.0f) return fail(MXFA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
     if (!isfinite(scale)) return fail(MXFA_ERR_INVALID_ARG, "scale must be finite");
