@@ -357,9 +357,11 @@ void fwd_bf16_kernel(const FwdParams p) {
     // Phase A, fused: S_{j+1} = K_{j+1} Q^T on the MFMAs while the vector
     // ALU turns S_j into P_j. After each MFMA one slice of the exponentials
     // (two elements), fenced so that the compiler keeps the interleave; the K
-    // operand reads run AHEAD MFMAs ahead.
+    // operand reads run AHEAD MFMAs ahead. `issue_v` (the next V tile's
+    // loads) goes out after MFMA kIssueV.
     auto qk_exp = [&](f32x16_t (&sn)[2], const char* kt_lds, f32x16_t (&sc)[2], uint32_t (&pk)[2][8],
-                      float& psb) __attribute__((always_inline)) {
+                      float& psb, auto&& issue_v) __attribute__((always_inline)) {
+        constexpr int kIssueV = 4;
         constexpr int NM = 2 * KSTEPS;  // MFMAs: m = 2*ks + kb
         constexpr int EPS = 32 / NM;    // exponentials per slice
         constexpr int AHEAD = 4;
@@ -388,6 +390,7 @@ void fwd_bf16_kernel(const FwdParams p) {
         for (int m = 0; m < NM; ++m) {
             if (m + AHEAD < NM) a[m + AHEAD] = rd(m + AHEAD);
             sn[m & 1] = mfma32x32x16(a[m], qreg[m >> 1], sn[m & 1]);
+            if (m == kIssueV) issue_v();
 #pragma unroll
             for (int e = 0; e < EPS; e += 2) {
                 const int idx = m * EPS + e;
@@ -506,18 +509,20 @@ void fwd_bf16_kernel(const FwdParams p) {
             char* const v_fill = P ? sV0 : sV1;
             const char* const v_use = P ? sV1 : sV0;
             const int kt = kt0 + j * BN;
-            // K(j+2) and V(j+1) both go out at the start of the step: their
-            // buffers were released by the previous step's barrier, and the
-            // wait at this step's end then finds them landed more often than
-            // when parts were issued inside the phases (3% faster on the
-            // causal and chunked prefill workloads).
+            // K(j+2) goes out at the start of the step and V(j+1) a few MFMAs
+            // into phase A (their buffers were released by the previous
+            // step's barrier): splitting the group's 32 KB burst of loads
+            // shortens each wave's issue stall (~1%), and V(j+1) is not read
+            // before the next step's phase B.
             if (j + 2 < ntiles) issue_b(Kseg, kt + 2 * BN, k_fill, loop_bytes(kt + 2 * BN));
-            if (j + 1 < ntiles) issue_b(Vseg, kt + BN, v_fill, loop_bytes(kt + BN));
+            auto issue_v = [&]() __attribute__((always_inline)) {
+                if (j + 1 < ntiles) issue_b(Vseg, kt + BN, v_fill, loop_bytes(kt + BN));
+            };
             uint32_t pk[2][8];
             if constexpr (kNext) {
                 // Phase A: S_{j+1} = K_{j+1} Q^T on the MFMAs, P_j on the vector ALU.
                 float psb;
-                const float psum = qk_exp(s_next, k_use, s_cur, pk, psb);
+                const float psum = qk_exp(s_next, k_use, s_cur, pk, psb, issue_v);
                 settle(s_cur, pk, psum, psb);
                 // Phase B: O += V_j P_j on the MFMAs, mask + max of S_{j+1} on the vector ALU.
                 if (tile_full(kt + BN))
@@ -527,6 +532,7 @@ void fwd_bf16_kernel(const FwdParams p) {
                 else
                     pv_mask(mask2{}, pk, v_use, s_next, kt + BN);
             } else {
+                issue_v();  // (no next tile: nothing to load)
                 float psb;
                 const float psum = exp_tile(s_cur, pk, psb);
                 settle(s_cur, pk, psum, psb);
