@@ -3,8 +3,9 @@
 Small problems compare every element; they span several q/k tiles with ragged
 tails, GQA, Sq != Sk (bottom-right causal), fully-masked rows, empty
 segments, windows and softcap. The five headline workloads run at full size
-in the launch configuration the bench times, compared on seeded sampled rows
-(every segment's first/last rows and q-tile edges included). Tolerances:
+in the launch configuration the bench times, and every one of their rows is
+compared with the oracle (the paged variant of the latent decode on seeded
+sampled rows, plus bit equality with the contiguous call). Tolerances:
 max |O - O_ref| <= 1e-5 (fp32) or 1e-2 (bf16), |LSE - LSE_ref| <= 1e-4.
 """
 from __future__ import annotations
@@ -735,6 +736,84 @@ def test_prefill_after_kernels_that_leave_other_data_in_lds():
             ref = (o.clone(), lse.clone())
         else:
             assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
+def _nan_latent_decode(d):
+    """A latent decode over an all-NaN cache, one work group per CU: it leaves NaN
+    in every byte of LDS its tiles and partial-score exchange use (160 KB per CU)."""
+    p = workloads.make_problem(3620, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=[1] * 128,
+                               lens_k=[512] * 128, shared_kv=True)
+    q = p["q"].to(d)
+    kv = torch.full_like(p["kv"], float("nan")).to(d)
+    cq, ck = p["cu_seqlens_q"].to(d), p["cu_seqlens_k"].to(d)
+
+    def run():
+        mx.mxfa_decode_splitkv(q, kv, cq, ck, 1, 512, head_dim_v=512, num_splits=2)
+
+    return run
+
+
+def test_decodes_after_kernels_that_leave_other_data_in_lds():
+    # The decode kernels also load each tile cooperatively (every wave a part),
+    # so the same rule holds: a tile is read only after a barrier that follows
+    # every wave's wait. Each decode runs right after a kernel that leaves NaN
+    # in the LDS of every CU (a latent decode over a NaN cache, and the prefill
+    # over NaN keys and values); its rows must be finite, match the oracle and
+    # repeat bit for bit.
+    d = dev()
+    dirty_decode = _nan_latent_decode(d)
+    pf = workloads.make_problem(3621, dtype="bf16", heads_q=16, heads_kv=16, d_qk=128, d_v=128, lens_q=[2048] * 4,
+                                lens_k=[2048] * 4, dense=True)
+    pq = pf["q"].to(d)
+    pk = torch.full_like(pf["k"], float("nan")).to(d)
+    pv = torch.full_like(pf["v"], float("nan")).to(d)
+
+    def dirty_prefill():
+        mx.mxfa_fwd(pq, pk, pv, causal=False)
+
+    scale_l = 1.0 / math.sqrt(576)
+    scale_g = 1.0 / math.sqrt(128)
+    lat = workloads.make_problem(3622, dtype="bf16", heads_q=16, heads_kv=1, d_qk=576, d_v=512, lens_q=[4, 4, 2],
+                                 lens_k=[1000, 129, 700], shared_kv=True)
+    f8 = _fp8_problem(3623, [4, 3], [900, 200], 16, 1)
+    pgp, pgt = _paged_problem(3624, [4, 4], [600, 333], 16, 1, 64)
+    gq = workloads.make_problem(3625, dtype="bf16", heads_q=32, heads_kv=4, d_qk=128, d_v=128, lens_q=[1, 2, 1],
+                                lens_k=[2000, 700, 129])
+    cases = {
+        "latent": lambda: _run_decode(lat, 16, True, (-1, -1), 0.0, 3, scale_l),
+        "fp8": lambda: _run_fp8(f8, True, (-1, -1), 0.0, 3, scale_l),
+        "paged": lambda: _run_paged(pgp, pgt, True, (-1, -1), 0.0, 3, scale_l),
+        "gqa": lambda: _run_gqa(gq, True, (-1, -1), 0.0, 3, scale_g),
+    }
+    import oracle
+
+    kv = to_np(lat["kv"])
+    ref_lat = oracle.attention_rows(to_np(lat["q"]), kv, kv[:, :, :512], lat["cu_seqlens_q"].numpy(),
+                                    lat["cu_seqlens_k"].numpy(), causal=True, scale=scale_l)[:2]
+    ref_f8 = oracle.attention_rows_fp8_latent(to_np(f8["q"]), f8["kv8"].numpy(), f8["kv_scale"],
+                                              f8["cu_seqlens_q"].numpy(), f8["cu_seqlens_k"].numpy(), d_v=512,
+                                              causal=True, scale=scale_l)[:2]
+    kvp, ckp = oracle.gather_paged(to_np(pgt["kv_cache"]), pgt["block_table"].numpy(), pgt["cache_seqlens"].numpy())
+    ref_pg = oracle.attention_rows(to_np(pgp["q"]), kvp, kvp[:, :, :512], pgp["cu_seqlens_q"].numpy(), ckp,
+                                   causal=True, scale=scale_l)[:2]
+    ref_gq = oracle_varlen(gq, causal=True, window=(-1, -1), softcap=0.0, scale=scale_g)[:2]
+    refs = {"latent": ref_lat, "fp8": ref_f8, "paged": ref_pg, "gqa": ref_gq}
+    for name, run in cases.items():
+        first = None
+        for rep, dirty in enumerate((dirty_decode, dirty_prefill, dirty_decode)):
+            print(f"[lds-reuse] {name} after {'decode' if dirty is dirty_decode else 'prefill'} (round {rep})",
+                  flush=True)
+            dirty()
+            o, lse = run()
+            assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), name
+            if first is None:
+                first = (o, lse)
+                o_ref, lse_ref = refs[name]
+                dv = o_ref.shape[-1]
+                compare(o.reshape(-1, dv), lse.T.reshape(-1), o_ref.reshape(-1, dv), lse_ref.reshape(-1), "bf16",
+                        name)
+            else:
+                assert np.array_equal(o, first[0]) and np.array_equal(lse, first[1]), name
 
 
 @pytest.mark.timeout(600)
