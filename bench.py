@@ -660,10 +660,10 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline: fp64 oracle on a sample of the prefill workload", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(PRIMARY, args.cpu_seconds)
-        # The same oracle on bounded samples of the packed GQA prefill and the
-        # latent decode (reported only; the headline figure is the prefill's).
+        # The same oracle on bounded samples of the other headline workloads
+        # (reported only; the headline figure is the prefill's).
         others = []
-        for name in ("varlen_gqa_causal_bf16", DECODE):
+        for name in ("single_head_f32", "varlen_gqa_causal_bf16", DECODE, "window_softcap_bf16"):
             print(f"[bench] cpu baseline: fp64 oracle on a sample of {name}", file=sys.stderr, flush=True)
             others.append(cpu_baseline(name, args.cpu_seconds / 2))
         line["cpu_baseline"]["others"] = others
