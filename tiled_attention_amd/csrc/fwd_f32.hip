@@ -17,11 +17,19 @@ namespace {
 constexpr int NTHREADS = 256;
 constexpr int LPR = 8;                    // lanes per query row
 constexpr int BM = kFwdF32Rows;           // 32 query rows per work group (NTHREADS / LPR)
-constexpr int BN = kFwdF32Keys;           // 32 keys per tile
 static_assert(BM == NTHREADS / LPR, "one row per LPR lanes");
+
+// Keys per tile: 128 at d = 64 (70 KB of LDS; the key range of a 128-token
+// problem is then one load round trip instead of four), 32 at d = 128, where
+// the row's q and accumulator already take 256 registers.
+template <int D>
+constexpr int tile_keys() {
+    return D == 64 ? 128 : kFwdF32Keys;
+}
 
 template <int D, bool kCap>
 __global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
+    constexpr int BN = tile_keys<D>();
     constexpr int RS = D + 4;  // padded LDS row (floats)
     __shared__ __attribute__((aligned(16))) float sK[BN * RS];
     __shared__ __attribute__((aligned(16))) float sV[BN * RS];
@@ -86,19 +94,31 @@ __global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
     if (kv_lo <= kv_hi) {
         for (int kt = kv_lo & ~(BN - 1); kt <= kv_hi; kt += BN) {
             __syncthreads();
-            for (int c = tid; c < BN * D / 4; c += NTHREADS) {
+            // Every 16-byte chunk of the tile's K and V rows: all loads of
+            // this thread are issued before its first LDS write, so the tile
+            // costs one memory round trip.
+            constexpr int NLD = BN * D / 4 / NTHREADS;
+            static_assert(NLD * NTHREADS * 4 == BN * D, "whole chunks per thread");
+            f32x4_t kk[NLD], vv[NLD];
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int c = n * NTHREADS + tid;
+                const int key = kt + c / (D / 4);
+                kk[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                vv[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                if (key < sk) {
+                    const long long g = (long long)(k_start + key) * kv_tok + (long long)kvh * D + (c % (D / 4)) * 4;
+                    kk[n] = *reinterpret_cast<const f32x4_t*>(K + g);
+                    vv[n] = *reinterpret_cast<const f32x4_t*>(V + g);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NLD; ++n) {
+                const int c = n * NTHREADS + tid;
                 const int r = c / (D / 4);
                 const int ch = c % (D / 4);
-                const int key = kt + r;
-                f32x4_t kk = {0.f, 0.f, 0.f, 0.f};
-                f32x4_t vv = {0.f, 0.f, 0.f, 0.f};
-                if (key < sk) {
-                    const long long g = (long long)(k_start + key) * kv_tok + (long long)kvh * D + ch * 4;
-                    kk = *reinterpret_cast<const f32x4_t*>(K + g);
-                    vv = *reinterpret_cast<const f32x4_t*>(V + g);
-                }
-                *reinterpret_cast<f32x4_t*>(&sK[r * RS + ch * 4]) = kk;
-                *reinterpret_cast<f32x4_t*>(&sV[r * RS + ch * 4]) = vv;
+                *reinterpret_cast<f32x4_t*>(&sK[r * RS + ch * 4]) = kk[n];
+                *reinterpret_cast<f32x4_t*>(&sV[r * RS + ch * 4]) = vv[n];
             }
             __syncthreads();
 
