@@ -192,30 +192,54 @@ void decode_split_kernel(const DecodeParams p) {
         return (uint32_t)(row * (int)(kv_tok_stride * 2) + c * 16);
     };
     const char* KVseg = static_cast<const char*>(p.kv) + ((long long)k_start * kv_tok_stride + (long long)g * DQK) * ESZ;
-    // Paged cache: physical page of the tile at key kt (a tile never
-    // straddles a page, pages holding a multiple of BN keys); 0 for tiles
-    // past the keys, which are never read. Read one step before its use.
-    // The table is read through the constant address space: it is not
-    // written while the kernel runs, and so the read becomes a scalar load,
-    // kept out of the vector-memory count that the stage waits rely on.
+    // Paged cache: physical page of a tile (a tile never straddles a page,
+    // pages holding a multiple of BN keys) and the tile's first row in it;
+    // page 0 for tiles past the keys, which are never read. Read one step
+    // before its use. The table is read through the constant address space:
+    // it is not written while the kernel runs, and so the read becomes a
+    // scalar load, kept out of the vector-memory count that the stage waits
+    // rely on. Tiles are looked up once each, in key order, so a cursor
+    // (table index, row in the page) advanced by BN replaces a division by
+    // the page size per tile.
     using ConstI32 = const __attribute__((address_space(4))) int32_t;
-    auto page_of = [&](int kt) __attribute__((always_inline)) -> int {
-        if (!kPaged || kt > hi) return 0;
-        const ConstI32* tab = (const ConstI32*)p.block_table;
-        return tab[(long long)b * p.max_pages + kt / p.page_size];
+    struct PageRef {
+        int phys;  // physical page
+        int off;   // the tile's first row within it
+    };
+    int pc_idx = 0, pc_off = 0;  // cursor: the next tile to look up
+    auto page_cursor_at = [&](int kt) __attribute__((always_inline)) {
+        if constexpr (kPaged) {
+            pc_idx = kt / p.page_size;
+            pc_off = kt - pc_idx * p.page_size;
+        }
+    };
+    auto next_page = [&](int kt) __attribute__((always_inline)) -> PageRef {
+        PageRef r{0, pc_off};
+        if constexpr (kPaged) {
+            if (kt <= hi) {
+                const ConstI32* tab = (const ConstI32*)p.block_table;
+                r.phys = tab[(long long)b * p.max_pages + pc_idx];
+            }
+            pc_off += BN;
+            if (pc_off == p.page_size) {
+                pc_off = 0;
+                ++pc_idx;
+            }
+        }
+        return r;
     };
     // Buffer resource over the tile at key kt: its rows up to the last key
     // (rows past it read as zeros). Tiles past the split's last key, and
     // tiles whose page number lies outside the cache, get a resource of zero
     // bytes: their loads return zeros without touching memory.
-    auto tile_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+    auto tile_rsrc = [&](int kt, PageRef pr) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
         long long bytes = ((long long)(sk - kt - 1) * kv_tok_stride + DQK) * ESZ;
         const char* base = KVseg + (long long)kt * kv_tok_stride * ESZ;
         if (kPaged) {
-            if ((unsigned)phys >= (unsigned)p.num_pages) bytes = 0;
+            if ((unsigned)pr.phys >= (unsigned)p.num_pages) bytes = 0;
             else
                 base = static_cast<const char*>(p.kv) +
-                       (((long long)phys * p.page_size + kt % p.page_size) * kv_tok_stride + (long long)g * DQK) * ESZ;
+                       (((long long)pr.phys * p.page_size + pr.off) * kv_tok_stride + (long long)g * DQK) * ESZ;
         }
         if (kt > hi) bytes = 0;
         if (bytes > 0x7fffffffLL) bytes = 0x7fffffffLL;
@@ -229,7 +253,7 @@ void decode_split_kernel(const DecodeParams p) {
         for (int n = n0; n < n1; ++n) buffer_load_lds16(r, stage + (n * NTHREADS + w * 64) * 16, goff(n));
     };
     auto issue_tile = [&](int kt, char* stage) __attribute__((always_inline)) {
-        issue_part(tile_rsrc(kt, page_of(kt)), stage, 0, LOADS);
+        issue_part(tile_rsrc(kt, next_page(kt)), stage, 0, LOADS);
     };
     // fp8 rows take another way into LDS: 16-byte chunks (16 values) are
     // loaded into registers three tiles ahead, converted to bf16 (exact: every
@@ -255,7 +279,7 @@ void decode_split_kernel(const DecodeParams p) {
         u32x4_t v[LOADS8];
     };
     auto load8 = [&](int kt, Raw8& r) __attribute__((always_inline)) {
-        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt, 0);
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(kt, PageRef{0, 0});
 #pragma unroll
         for (int n = 0; n < LOADS8; ++n) r.v[n] = buffer_load16(rs, go8[n], 0);
     };
@@ -496,8 +520,8 @@ void decode_split_kernel(const DecodeParams p) {
         const int kt_last = kt0 + (ntiles - 1) * BN;
         long long last64 = ((long long)(sk - kt_last - 1) * kv_tok_stride + DQK) * ESZ;
         const uint32_t last_bytes = (uint32_t)(last64 < (long long)span ? last64 : (long long)span);
-        auto loop_rsrc = [&](int kt, int phys) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
-            if constexpr (kPaged) return tile_rsrc(kt, phys);
+        auto loop_rsrc = [&](int kt, PageRef pr) __attribute__((always_inline)) -> __amdgpu_buffer_rsrc_t {
+            if constexpr (kPaged) return tile_rsrc(kt, pr);
             const uint32_t bytes = kt > hi ? 0u : (kt == kt_last ? last_bytes : span);
             return make_rsrc(bytes ? KVseg + (long long)kt * kv_tok_stride * ESZ : KVseg, bytes);
         };
@@ -510,10 +534,11 @@ void decode_split_kernel(const DecodeParams p) {
                 xs[w][q4][lane] = f32x4_t{s_mine[4 * q4], s_mine[4 * q4 + 1], s_mine[4 * q4 + 2], s_mine[4 * q4 + 3]};
         };
       if constexpr (!kFp8) {
+        page_cursor_at(kt0);
         issue_tile(kt0, sT0);
         issue_tile(kt0 + BN, sT1);
         issue_tile(kt0 + 2 * BN, sT2);
-        int phys_fill = page_of(kt0 + 3 * BN);  // page of the tile the next step issues
+        PageRef pg_fill = next_page(kt0 + 3 * BN);  // page of the tile the next step issues
         asm volatile("s_waitcnt vmcnt(18)" ::: "memory");  // this wave's loads of tile 0
         lds_barrier();
         s_mine = qk_tile(sT0);
@@ -537,13 +562,13 @@ void decode_split_kernel(const DecodeParams p) {
             const int kt_fill = kt0 + (j + 3) * BN;  // tile j+3 -> the stage of tile j-1
             uint32_t pk[8];
             float alpha = 1.0f;
-            const __amdgpu_buffer_rsrc_t rfill = loop_rsrc(kt_fill, phys_fill);
-            phys_fill = page_of(kt_fill + BN);
+            const __amdgpu_buffer_rsrc_t rfill = loop_rsrc(kt_fill, pg_fill);
+            pg_fill = next_page(kt_fill + BN);
             // Wait for the page-table read here, where no LDS read is in
             // flight: the scalar load shares the LDS wait counter and returns
             // out of order, so while it is pending every LDS wait of the step
             // would have to drain all reads.
-            if constexpr (kPaged) asm volatile("" : "+s"(phys_fill));
+            if constexpr (kPaged) asm volatile("" : "+s"(pg_fill.phys));
             issue_part(rfill, prv, 0, 3);
             // Every wave runs the same code (a row block past the group's rows
             // sees no key, so its results stay zero and are never read): the
@@ -610,7 +635,7 @@ void decode_split_kernel(const DecodeParams p) {
             char* const fill = S == 0 ? sT2 : S == 1 ? sT0 : sT1;
             uint32_t pk[8];
             float alpha = 1.0f;
-            const __amdgpu_buffer_rsrc_t rs = loop_rsrc(kt0 + (j + 3) * BN, 0);
+            const __amdgpu_buffer_rsrc_t rs = loop_rsrc(kt0 + (j + 3) * BN, PageRef{0, 0});
             load8_part(rs, rl, 0, 2);
             s_mine = qk_softmax(nxt, s_mine, kt0 + j * BN, pk, alpha, (j & 1) ? sS1 : sS,
                                 [&]() __attribute__((always_inline)) { load8_part(rs, rl, 2, 4); });
