@@ -2,22 +2,31 @@
 //
 // The same tiled online softmax as the bf16 kernel (oxillama-runtime 0.1.0
 // page, src/flash_attention.rs, flash_attention), on the vector ALU in fp32 so
-// that fp32 inputs keep fp32 products. Work group: 256 threads for 32 query
-// rows; the 8 lanes of a row each take every 8th key of a tile and keep their
-// own running (max, sum, accumulator); the 8 partial states of a row are
-// merged with the max/sum correction at the end (the split combine of the
-// kernelbot amd-mixed-mla submission 588924 page, _reduce_splitk, within a
-// row). K/V tiles are staged in LDS with padded rows, so the 8 different
-// keys a wave reads at once fall on different banks.
+// that fp32 inputs keep fp32 products. Work group: 32 query rows, L lanes per
+// row (L = 16 at d = 64, 8 at d = 128); the L lanes of a row each take every
+// L-th key of a tile and keep their own running (max, sum, accumulator); the
+// L partial states of a row are merged with the max/sum correction at the end
+// (the split combine of the kernelbot amd-mixed-mla submission 588924 page,
+// _reduce_splitk, within a row). K/V tiles are staged in LDS with padded
+// rows, so the different keys a wave reads at once fall on different banks.
 #include "mxfa_device.h"
 
 namespace mxfa {
 namespace {
 
-constexpr int NTHREADS = 256;
-constexpr int LPR = 8;                    // lanes per query row
-constexpr int BM = kFwdF32Rows;           // 32 query rows per work group (NTHREADS / LPR)
-static_assert(BM == NTHREADS / LPR, "one row per LPR lanes");
+constexpr int BM = kFwdF32Rows;  // 32 query rows per work group
+
+// Lanes per query row: 16 at d = 64 (512 threads; each lane's dependent FMA
+// chain over a tile is half as long), 8 at d = 128 (256 threads), where the
+// row's q and accumulator already take 256 registers per lane.
+template <int D>
+constexpr int lanes_per_row() {
+    return D == 64 ? 16 : 8;
+}
+template <int D>
+constexpr int threads_of() {
+    return BM * lanes_per_row<D>();
+}
 
 // Keys per tile: 128 at d = 64 (70 KB of LDS; the key range of a 128-token
 // problem is then one load round trip instead of four), 32 at d = 128, where
@@ -28,7 +37,9 @@ constexpr int tile_keys() {
 }
 
 template <int D, bool kCap>
-__global__ __launch_bounds__(NTHREADS) void fwd_f32_kernel(const FwdParams p) {
+__global__ __launch_bounds__(threads_of<D>()) void fwd_f32_kernel(const FwdParams p) {
+    constexpr int LPR = lanes_per_row<D>();
+    constexpr int NTHREADS = threads_of<D>();
     constexpr int BN = tile_keys<D>();
     constexpr int RS = D + 4;  // padded LDS row (floats)
     __shared__ __attribute__((aligned(16))) float sK[BN * RS];
@@ -211,9 +222,9 @@ hipError_t launch_d(const FwdParams& args, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, true>), dim3((unsigned)grid), dim3(threads_of<D>()), 0, stream, p);
     else
-        hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(NTHREADS), 0, stream, p);
+        hipLaunchKernelGGL((fwd_f32_kernel<D, false>), dim3((unsigned)grid), dim3(threads_of<D>()), 0, stream, p);
     return hipGetLastError();
 }
 
